@@ -1,0 +1,192 @@
+"""Quantized attention forward: scores, online softmax, FP8 P, PV, epilogue.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Source: diffusers issue #15014, "gfx1201 (RDNA4) SageAttention attention
+backend: aiter package or Hub kernel?", problem statement: INT8 QK^T and FP8
+PV with FP32 accumulation, bf16 [B, S, H, 128] inputs, no mask, non-causal,
+operation ``gfx1201_sage_attention(q, k, v, softmax_scale)``; diffusers PR
+#15060, "What does this PR do?": no LSE is returned.
+
+The method is an approximation, so this module follows its steps rather than
+exact attention (``exact_attention_fp64`` is the separate exact reference).
+Readings taken where the pages are silent, in step order:
+
+1. Scores A = q8 . k8^T are exact integers (|A| <= 128*127^2 < 2^24).
+2. Dequantization in the log2 domain: c = fl32(fl32(softmax_scale) *
+   fl32(log2 e)), f = fl32(fl32(q_scale * k_scale) * c) per (query block,
+   key block), t = fl32(float(A) * f).
+3. Online softmax over consecutive key tiles of ``bn`` keys, in key order (a
+   flash-style forward streams K/V tiles; the tile width is the kernel's and
+   is passed in). Per query row and tile tau:
+   m_tau = max(m_{tau-1}, max_{j in tau} t_j)  (m_0 = -inf).
+4. P with the fixed 448 scale, folded into the exponent: m2_tau =
+   fl32(m_tau - fl32(log2 448)); arg_j = fl32(A_j * f - m2_tau) (the exact
+   real value rounded once, i.e. a fused multiply-add); P'_j = fl32(2^arg_j),
+   so P'_j = 448 * 2^(t_j - m_tau) up to rounding and lies in (0, 448].
+   p8_j = E4M3FN(P'_j). The row sum l accumulates the fp32 P'_j.
+5. Across tiles, partial sums are combined with the factors 2^(m2_tau -
+   m2_T) of the final tile T (here in float64; the kernel rescales its fp32
+   accumulators as it goes, which agrees to fp32 rounding).
+6. PV: acc[c] = sum_j dec(p8_j) * dec(v8[j, c]); products of two FP8 values
+   are exact. Epilogue: O[c] = bf16(acc[c] * v_scale[c] / l), formed in
+   float64 and rounded once.
+
+Where the exact value of step 4's subtraction is not representable in float64
+(an exponent gap above ~8 binades between the two terms) the float64 result
+is rounded a second time to fp32; the two roundings disagree with the single
+rounding only when the first lands exactly on an fp32 midpoint.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .formats import bf16_round_f64, f32, fp8_e4m3fn_decode, fp8_e4m3fn_encode
+from .quant import QK_BLOCK, quant_qk, quant_v
+
+LOG2E = np.float32(math.log2(math.e))
+LOG2_448 = np.float32(math.log2(448.0))
+
+
+def exp2_scale(softmax_scale: float) -> np.float32:
+    """c = fl32(fl32(softmax_scale) * fl32(log2 e)): scores to the log2 domain."""
+    return (np.float32(softmax_scale) * LOG2E).astype(np.float32)
+
+
+def qk_scores(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
+    """Exact integer scores A = q8 . k8^T as int64.
+
+    Computed by a float64 matrix product: every partial sum is an integer of
+    magnitude below 2^53, so the product is exact in any summation order.
+    """
+    a = np.asarray(q8, dtype=np.float64) @ np.asarray(k8, dtype=np.float64).T
+    return a.astype(np.int64)
+
+
+def online_softmax_pv(x: np.ndarray, vals: np.ndarray, bn: int, quantized: bool = True,
+                      n_valid: int | None = None):
+    """Tile-scheduled online softmax followed by PV, for a set of query rows.
+
+    x:    float64 [R, S] exact scores in the log2 domain (A * f, step 2
+          without the final rounding; for the unquantized path any real
+          scores times log2 e).
+    vals: float64 [S, D] values multiplying P (decoded FP8 V codes when
+          ``quantized``, plain V otherwise).
+    bn:   key tile width.
+    quantized: True follows steps 3-5 with fp32 roundings and FP8 P;
+          False is the same tile loop in float64 with P = 2^(x - m), no
+          rounding and no encoding (used to pin the loop against textbook
+          softmax attention).
+    n_valid: keys at index >= n_valid are masked (count as -inf).
+
+    Returns (acc float64 [R, D], l float64 [R]); the output is acc / l
+    (times v_scale for the quantized path).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R, S = x.shape
+    if n_valid is None:
+        n_valid = S
+    ntiles = (S + bn - 1) // bn
+    m_prev = np.full(R, -np.inf)
+    shifts = []      # per tile: exponent offset used for that tile's P
+    l_parts = []
+    acc_parts = []
+    for tau in range(ntiles):
+        j0, j1 = tau * bn, min(S, (tau + 1) * bn)
+        j1v = min(j1, n_valid)
+        if j1v <= j0:
+            break
+        xt = x[:, j0:j1v]
+        if quantized:
+            t = f32(xt)                                      # fl32(A * f)
+            m = np.maximum(m_prev, t.max(axis=1).astype(np.float64))
+            m2 = (m.astype(np.float32) - LOG2_448).astype(np.float32)
+            arg = f32(xt - m2.astype(np.float64)[:, None])   # fma, one rounding
+            p = f32(np.exp2(arg.astype(np.float64)))         # P' in fp32
+            p_used = fp8_e4m3fn_decode(fp8_e4m3fn_encode(p))  # dec(E4M3FN(P'))
+            shift = m2.astype(np.float64)
+            l_t = p.astype(np.float64).sum(axis=1)
+        else:
+            m = np.maximum(m_prev, xt.max(axis=1))
+            p = np.exp2(xt - m[:, None])
+            p_used = p
+            shift = m
+            l_t = p.sum(axis=1)
+        acc_t = p_used @ np.asarray(vals[j0:j1v], dtype=np.float64)
+        shifts.append(shift)
+        l_parts.append(l_t)
+        acc_parts.append(acc_t)
+        m_prev = m
+    final = shifts[-1]
+    l = np.zeros(R)
+    acc = np.zeros((R, vals.shape[1]))
+    for shift, l_t, acc_t in zip(shifts, l_parts, acc_parts):
+        w = np.exp2(shift - final)
+        l += w * l_t
+        acc += w[:, None] * acc_t
+    return acc, l
+
+
+def attention_head(q8, q_scale, k8, k_scale, v8, v_scale, softmax_scale, bn,
+                   rows=None, n_valid=None, return_f64=False):
+    """Quantized attention output for one (batch, head).
+
+    q8, k8: int8 [S, D]; q_scale, k_scale: fp32 [ceil(S/32)];
+    v8: uint8 E4M3FN codes [S, D] (natural key order); v_scale: fp32 [D].
+    rows: query indices to compute (default: all).
+    Returns bf16-valued float32 [len(rows), D] (and the float64 value before
+    the final rounding if ``return_f64``).
+    """
+    S = k8.shape[0]
+    if rows is None:
+        rows = np.arange(q8.shape[0])
+    rows = np.asarray(rows)
+    c = exp2_scale(softmax_scale)
+    A = qk_scores(q8[rows], k8)                                  # [R, S] exact
+    f_blocks = f32(f32(q_scale[rows // QK_BLOCK][:, None].astype(np.float32)
+                       * k_scale[None, :].astype(np.float32)) * c)  # [R, nbk]
+    f_keys = f_blocks[:, np.arange(S) // QK_BLOCK]               # [R, S] fp32
+    x = A.astype(np.float64) * f_keys.astype(np.float64)        # exact
+    vals = fp8_e4m3fn_decode(v8)
+    acc, l = online_softmax_pv(x, vals, bn, quantized=True, n_valid=n_valid)
+    o64 = acc * np.asarray(v_scale, dtype=np.float64)[None, :] / l[:, None]
+    o = bf16_round_f64(o64)
+    return (o, o64) if return_f64 else o
+
+
+def sage_attention(q, k, v, softmax_scale, bn, rows=None, heads=None):
+    """Whole method on bf16-valued float32 [B, S, H, D] inputs.
+
+    Returns O as float32 [B, S, H, D] holding bf16 values. With ``rows``
+    (query indices) and/or ``heads`` (list of (b, h)), only those are
+    computed and the rest of the output is NaN.
+    """
+    B, S, H, D = q.shape
+    q8, qs = quant_qk(q)
+    k8, ks = quant_qk(k)
+    v8, vs = quant_v(v)
+    out = np.full((B, S, H, D), np.nan, dtype=np.float32)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    rws = np.arange(S) if rows is None else np.asarray(rows)
+    for b, h in pairs:
+        out[b, rws, h, :] = attention_head(q8[b, h], qs[b, h], k8[b, h], ks[b, h],
+                                           v8[b, h], vs[b, h], softmax_scale, bn, rows=rws)
+    return out
+
+
+def exact_attention_fp64(q, k, v, softmax_scale):
+    """Textbook softmax(q k^T * scale) v per (b, h), in float64; [B, S, H, D]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, S, H, D = q.shape
+    out = np.empty((B, S, H, D))
+    for b in range(B):
+        for h in range(H):
+            s = (q[b, :, h, :] @ k[b, :, h, :].T) * softmax_scale
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            out[b, :, h, :] = (p @ v[b, :, h, :]) / p.sum(axis=1, keepdims=True)
+    return out

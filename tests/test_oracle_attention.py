@@ -1,0 +1,304 @@
+"""Pins for the oracle's attention steps.
+
+Each pin is chosen so that a plausible mistake in the oracle (a dropped
+rescale, a wrong tile boundary, a transposed operand, a wrong scale index, a
+sign error in the exponent) fails at least one of them:
+
+* exact integer scores: int64 reference vs the float64 product;
+* the tile loop with quantization switched off equals textbook fp64 softmax
+  attention to 1e-12, at several tile widths and ragged tails;
+* the whole oracle is within cosine 0.99 of exact fp64 attention;
+* row sums: V = 1 gives O = 1 (exactly in the unquantized loop, within the
+  FP8 bound when quantized);
+* invariances: joint K/V row permutations inside a 32-row block, Q row
+  permutations inside a block, power-of-two scalings;
+* closed forms: K = 0 (O = mean of dequantized V), V = 0, one dominant key;
+* the masked tail equals the unpadded computation;
+* an independent scalar brute-force implementation on tiny inputs agrees
+  bit for bit.
+"""
+import math
+import struct
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import (
+    attention_head,
+    exact_attention_fp64,
+    fp8_e4m3fn_decode,
+    online_softmax_pv,
+    qk_scores,
+    quant_qk,
+    quant_v,
+    sage_attention,
+)
+
+SCALE = 1.0 / math.sqrt(128)
+
+
+def _cos(a, b):
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def _head_inputs(q, k, v, b=0, h=0):
+    q8, qs = quant_qk(q)
+    k8, ks = quant_qk(k)
+    v8, vs = quant_v(v)
+    return q8[b, h], qs[b, h], k8[b, h], ks[b, h], v8[b, h], vs[b, h]
+
+
+def test_scores_exact_integer():
+    rng = np.random.default_rng(3)
+    q8 = rng.integers(-127, 128, size=(70, 128)).astype(np.int8)
+    k8 = rng.integers(-127, 128, size=(90, 128)).astype(np.int8)
+    ref = np.einsum("ic,jc->ij", q8.astype(np.int64), k8.astype(np.int64))
+    assert np.array_equal(qk_scores(q8, k8), ref)
+    extreme = np.full((2, 128), 127, dtype=np.int8)
+    extreme[1] = -127
+    assert qk_scores(extreme, extreme)[0, 0] == 128 * 127 * 127 < 2 ** 24
+
+
+@pytest.mark.parametrize("S,bn,n_valid", [(256, 64, None), (200, 64, None), (256, 32, None),
+                                          (300, 128, None), (256, 128, 201)])
+def test_unquantized_tile_loop_is_textbook_softmax(S, bn, n_valid):
+    rng = np.random.default_rng(S + bn)
+    q = rng.standard_normal((1, S, 1, 128)) * 2.0
+    k = rng.standard_normal((1, S, 1, 128))
+    v = rng.standard_normal((1, S, 1, 128))
+    nv = S if n_valid is None else n_valid
+    x = (q[0, :, 0] @ k[0, :, 0].T) * SCALE * math.log2(math.e)
+    acc, l = online_softmax_pv(x, v[0, :, 0], bn, quantized=False, n_valid=n_valid)
+    ref = exact_attention_fp64(q[:, :, :, :], k[:, :nv], v[:, :nv], SCALE)
+    # exact_attention_fp64 needs equal Q/K lengths only for its loops; emulate
+    s = (q[0, :, 0] @ k[0, :nv, 0].T) * SCALE
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    ref = (p @ v[0, :nv, 0]) / p.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(acc / l[:, None] - ref)) < 1e-12
+
+
+def test_unquantized_row_sum_is_one():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((64, 300)) * 20
+    acc, l = online_softmax_pv(x, np.ones((300, 4)), 64, quantized=False)
+    assert np.max(np.abs(acc / l[:, None] - 1.0)) < 1e-12
+
+
+def test_quantized_row_sum_within_fp8_bound():
+    # V constant per channel: v8 = 448 everywhere, so O / v = sum dec(p8) / sum P'
+    q, k, _ = workloads.generate(1, S=512, H=1)
+    v = np.ones_like(q) * np.float32(0.75)
+    args = _head_inputs(q, k, v)
+    o, o64 = attention_head(*args, SCALE, 128, return_f64=True)
+    r = o64 / 0.75
+    # |dec(E(P')) - P'| <= max(2^-4 P', 2^-10) per key, and l >= 448
+    bound = 2.0 ** -4 + 512 * 2.0 ** -10 / 448
+    assert np.all(np.abs(r - 1) <= bound)
+    # the relative FP8 noise averages out: the mean ratio is within 1%
+    assert abs(r.mean() - 1) < 1e-2
+
+
+def test_oracle_vs_exact_attention_config1():
+    cfg = workloads.config(1)
+    q, k, v = workloads.generate(1)
+    for bn in (64, 128):
+        o = sage_attention(q, k, v, cfg.softmax_scale, bn)
+        e = exact_attention_fp64(q, k, v, cfg.softmax_scale)
+        c = _cos(o, e)
+        assert c >= 0.99
+        assert c > 0.998      # FP8 P and V noise floor, about 0.9993 here
+
+
+def test_oracle_vs_exact_attention_structured_recipes():
+    for idx in (2, 3, 5):
+        cfg = workloads.config(idx)
+        q, k, v = workloads.generate(idx, S=512, H=2, B=1)
+        o = sage_attention(q, k, v, cfg.softmax_scale, 128)
+        e = exact_attention_fp64(q, k, v, cfg.softmax_scale)
+        assert _cos(o, e) >= 0.99, idx
+
+
+def test_joint_kv_permutation_inside_block_invariance():
+    q, k, v = workloads.generate(2, S=256, H=1, seed=21)
+    args = _head_inputs(q, k, v)
+    o, o64 = attention_head(*args, SCALE, 64, return_f64=True)
+    rng = np.random.default_rng(0)
+    perm = np.arange(256)
+    for blk in range(8):
+        perm[32 * blk:32 * blk + 32] = 32 * blk + rng.permutation(32)
+    kp, vp = k[:, perm], v[:, perm]
+    args_p = _head_inputs(q, kp, vp)
+    assert np.array_equal(args_p[3], args[3]) and np.array_equal(args_p[5], args[5])
+    op, op64 = attention_head(*args_p, SCALE, 64, return_f64=True)
+    assert np.max(np.abs(op64 - o64)) <= 1e-12 * np.max(np.abs(o64))
+    assert np.mean(op == o) > 0.999
+    # negative control: swapping rows across blocks changes the K block scales
+    # and the output
+    cross = np.arange(256)
+    cross[[5, 40]] = cross[[40, 5]]
+    cross[[70, 200]] = cross[[200, 70]]
+    k[0, 5] *= 3.0
+    args_c = _head_inputs(q, k[:, cross], v[:, cross])
+    args_0 = _head_inputs(q, k, v)
+    assert not np.array_equal(args_c[3], args_0[3])
+    oc64 = attention_head(*args_c, SCALE, 64, return_f64=True)[1]
+    o064 = attention_head(*args_0, SCALE, 64, return_f64=True)[1]
+    assert np.max(np.abs(oc64 - o064)) > 1e-6
+
+
+def test_query_permutation_inside_block_is_bit_exact():
+    q, k, v = workloads.generate(1, S=128, H=1, seed=22)
+    perm = np.arange(128)
+    perm[32:64] = 32 + np.random.default_rng(1).permutation(32)
+    o = attention_head(*_head_inputs(q, k, v), SCALE, 64)
+    op = attention_head(*_head_inputs(q[:, perm], k, v), SCALE, 64)
+    assert np.array_equal(op, o[perm])
+
+
+def test_power_of_two_scalings_are_exact():
+    q, k, v = workloads.generate(3, S=256, H=1, seed=23)
+    o = attention_head(*_head_inputs(q, k, v), SCALE, 64)
+    o_v = attention_head(*_head_inputs(q, k, v * np.float32(8.0)), SCALE, 64)
+    assert np.array_equal(o_v, o * np.float32(8.0))
+    o_q = attention_head(*_head_inputs(q * np.float32(4.0), k, v), SCALE / 4.0, 64)
+    assert np.array_equal(o_q, o)
+
+
+def test_closed_form_k_zero_gives_mean_of_dequantized_v():
+    q, _, v = workloads.generate(1, S=256, H=1, seed=24)
+    k = np.zeros_like(q)
+    q8, qs, k8, ks, v8, vs = _head_inputs(q, k, v)
+    _, o64 = attention_head(q8, qs, k8, ks, v8, vs, SCALE, 64, return_f64=True)
+    mean = (fp8_e4m3fn_decode(v8) * vs[None, :].astype(np.float64)).mean(axis=0)
+    # every P' is fl32(2^fl32(log2 448)) = 448 (1 +- 4e-7), encoded as 448
+    assert np.max(np.abs(o64 - mean[None, :])) <= 1e-6 * np.max(np.abs(mean))
+
+
+def test_closed_form_v_zero():
+    q, k, _ = workloads.generate(1, S=128, H=1, seed=25)
+    o = attention_head(*_head_inputs(q, k, np.zeros_like(q)), SCALE, 64)
+    assert np.all(o == 0)
+
+
+def test_closed_form_single_dominant_key():
+    q, k, v = workloads.generate(1, S=256, H=1, seed=26)
+    j = 77
+    q[0, :, 0, :] = workloads.bf16_round(np.sign(k[0, j, 0, :]) * 4.0)
+    k[0, j, 0, :] = workloads.bf16_round(np.sign(k[0, j, 0, :]) * 8.0)
+    q8, qs, k8, ks, v8, vs = _head_inputs(q, k, v)
+    _, o64 = attention_head(q8, qs, k8, ks, v8, vs, SCALE, 64, return_f64=True)
+    vj = fp8_e4m3fn_decode(v8[j]) * vs.astype(np.float64)
+    # every other key is 2^-400 below, so only key j carries weight; its P'
+    # is 448 * 2^d with |d| bounded by the fp32 roundings of the running max
+    # m (about 522 here, spacing 2^-14) and of m - log2 448
+    m = float(qk_scores(q8[:1], k8[j:j + 1])[0, 0]) * qs[0] * ks[j // 32] * SCALE * math.log2(math.e)
+    assert 512 <= m < 1024
+    bound = 2.0 ** -14 * math.log(2) + 2.0 ** -22
+    assert np.max(np.abs(o64 - vj[None, :])) <= bound * np.max(np.abs(vj))
+
+
+def test_masked_tail_equals_unpadded():
+    q, k, v = workloads.generate(5, S=80, H=1, B=1, seed=27)
+    o = attention_head(*_head_inputs(q, k, v), SCALE, 64)
+    pad = lambda x: np.concatenate([x, np.zeros((1, 48, 1, 128), np.float32)], axis=1)  # noqa: E731
+    q8, qs, k8, ks, v8, vs = _head_inputs(pad(q), pad(k), pad(v))
+    # zero rows change no block amax, so the quantized tensors agree on valid rows
+    q8u, qsu, k8u, ksu, v8u, vsu = _head_inputs(q, k, v)
+    assert np.array_equal(ks[:3], ksu) and np.array_equal(vs, vsu)
+    op = attention_head(q8, qs, k8, ks, v8, vs, SCALE, 64, rows=np.arange(80), n_valid=80)
+    assert np.array_equal(op, o)
+
+
+# ---------------------------------------------------------------------------
+# Independent scalar implementation (pure Python floats, tiny sizes only)
+
+def _f32(x):
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+_CODES = [(c, (c & 7) * 2.0 ** -9 if (c >> 3) == 0 else (1 + (c & 7) / 8) * 2.0 ** ((c >> 3) - 7))
+          for c in range(0x7F)]
+
+
+def _e4m3_scalar(y):
+    """Nearest E4M3FN code by exhaustive search; ties to the even code."""
+    a = min(abs(y), 448.0)
+    best = None
+    for c, val in _CODES:
+        d = abs(val - a)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c, val)
+    return math.copysign(best[2], y)
+
+
+def _bf16_scalar(x):
+    # nearest bf16 by checking the truncated value and the next one up
+    b = struct.unpack("I", struct.pack("f", _f32(x)))[0] & 0xFFFF0000
+    cands = []
+    for bb in (b - 0x10000, b, b + 0x10000):
+        if 0 <= bb < 2 ** 32:
+            cands.append(struct.unpack("f", struct.pack("I", bb))[0])
+    best = min(cands, key=lambda c: (abs(c - x), (struct.unpack("I", struct.pack("f", c))[0] >> 16) & 1))
+    return best
+
+
+def _scalar_method(q, k, v, scale, bn):
+    """One head, every step with scalar Python arithmetic."""
+    S, D = len(q), len(q[0])
+    def quant_rows(x):
+        out, scales = [], []
+        for t in range(0, S, 32):
+            blk = x[t:t + 32]
+            amax = max(abs(e) for row in blk for e in row)
+            inv = _f32(127.0 / amax) if amax > 0 else 0.0
+            scales.append(_f32(amax / 127.0) if amax > 0 else 0.0)
+            for row in blk:
+                out.append([max(-127, min(127, round(_f32(e * inv)))) for e in row])
+        return out, scales
+    q8, qs = quant_rows(q)
+    k8, ks = quant_rows(k)
+    vq, vs = [], []
+    for c in range(D):
+        amax = max(abs(v[j][c]) for j in range(S))
+        inv = _f32(448.0 / amax)
+        vs.append(_f32(amax / 448.0))
+        vq.append([_e4m3_scalar(_f32(v[j][c] * inv)) for j in range(S)])
+    c2 = _f32(_f32(scale) * _f32(math.log2(math.e)))
+    l448 = _f32(math.log2(448.0))
+    out = []
+    for i in range(S):
+        A = [sum(q8[i][d] * k8[j][d] for d in range(D)) for j in range(S)]
+        f = [_f32(_f32(qs[i // 32] * ks[j // 32]) * c2) for j in range(S)]
+        m = -math.inf
+        l, acc = 0.0, [0.0] * D
+        for j0 in range(0, S, bn):
+            js = range(j0, min(S, j0 + bn))
+            m_new = max(m, max(_f32(A[j] * f[j]) for j in js))
+            m2 = _f32(m_new - l448)
+            if m != -math.inf:
+                m2_old = _f32(m - l448)
+                w = 2.0 ** (m2_old - m2)
+                l *= w
+                acc = [a * w for a in acc]
+            for j in js:
+                p = _f32(2.0 ** _f32(A[j] * f[j] - m2))
+                l += p
+                p8 = _e4m3_scalar(p)
+                for c in range(D):
+                    acc[c] += p8 * vq[c][j]
+            m = m_new
+        out.append([_bf16_scalar(acc[c] * vs[c] / l) for c in range(D)])
+    return out
+
+
+@pytest.mark.parametrize("S,bn", [(40, 32), (96, 64)])
+def test_scalar_bruteforce_agrees(S, bn):
+    q, k, v = workloads.generate(3, S=S, H=1, seed=30 + S)
+    ref = np.array(_scalar_method(q[0, :, 0].tolist(), k[0, :, 0].tolist(), v[0, :, 0].tolist(),
+                                  SCALE, bn), dtype=np.float32)
+    got = sage_attention(q, k, v, SCALE, bn)[0, :, 0]
+    assert np.mean(got == ref) > 0.999
+    assert np.max(np.abs(got - ref)) <= 2 ** -7 * np.max(np.abs(ref))
