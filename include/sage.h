@@ -1,0 +1,164 @@
+/*
+ * sage.h - C ABI of the MI355X (gfx950) SageAttention-style quantized
+ * attention forward.
+ *
+ * What it computes (diffusers issue #15014, "gfx1201 (RDNA4) SageAttention
+ * attention backend: aiter package or Hub kernel?", problem statement): the
+ * forward of softmax(Q K^T * softmax_scale) V with INT8 QK^T and FP8 PV, FP32
+ * accumulation, Q and K quantized per 32-row block and V per channel, on bf16
+ * [B, S, H, 128] inputs of equal shape, with no mask and no causality. The
+ * call there is gfx1201_sage_attention(q, k, v, softmax_scale). Inference
+ * only, and no log-sum-exp is returned (diffusers PR #15060, "Add
+ * aiter_sage_hub attention backend for AMD RDNA4 (gfx1201)", section "What
+ * does this PR do?"). Unsupported inputs are rejected with an error code
+ * rather than served differently (the issue's "Describe the solution you'd
+ * like": reject with a clear error); a caller may fall back on its own.
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer is a device pointer owned by the caller. The
+ *     library never allocates, frees or synchronizes device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns before it completes;
+ *     results are valid after the caller synchronizes that stream.
+ *   - All argument checks run on the host before any launch; a failing check
+ *     returns its code and touches no memory. Launch failures return
+ *     SAGE_ERR_HIP. sage_last_error() gives a thread-local detail string.
+ *   - No global mutable state besides that string: calls are thread-safe;
+ *     calls that share output or workspace buffers must be ordered by the
+ *     caller.
+ *   - Sizes: B, S, H >= 1, D == 128, B*H*S_pad*128 < 2^62.
+ *   - Inputs containing NaN/Inf, or whose scaled scores overflow fp32, are
+ *     outside the contract (no guarantee on the output).
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  SAGE_ERR_SHAPE = 2,       /* B, S or H < 1, or sizes overflow               */
+  SAGE_ERR_UNSUPPORTED = 3, /* D != 128 (the only head size of the method)    */
+  SAGE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
+  SAGE_ERR_WORKSPACE = 5,   /* workspace/scratch smaller than required        */
+  SAGE_ERR_HIP = 6,         /* a HIP launch failed                            */
+  SAGE_ERR_RANGE = 7        /* debug-dump window outside the tensor           */
+} sage_status;
+
+/* ABI version of this header (incremented on any incompatible change). */
+int sage_abi_version(void);
+
+/* Static name of a status code. */
+const char* sage_status_str(int status);
+
+/* Thread-local text describing the last failing call on this thread. */
+const char* sage_last_error(void);
+
+/* Key-tile width BN of sage_attn_fwd. The online softmax rescales once per
+ * tile, and P is quantized relative to the running row max after each tile,
+ * so the result depends on BN; a reference implementation needs it. */
+int sage_kv_tile(void);
+
+/* Padded sequence length of the quantized layouts: S rounded up to a
+ * multiple of 256. Padded rows/keys hold zeros and are masked. */
+int64_t sage_seq_pad(int64_t S);
+
+/* Bytes of scratch sage_quant_v needs (per-chunk partial maxima). */
+size_t sage_quant_v_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
+
+/* Bytes of workspace sage_attention needs: the quantized Q, K, V, their
+ * scales and sage_quant_v's scratch, each 256-byte aligned. 0 on bad sizes. */
+size_t sage_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
+
+/*
+ * sage_quant_qk - INT8 quantization of Q or K per 32-row block (issue #15014,
+ * problem statement: "Q/K are quantized per 32-row block").
+ *   x       bf16 [B, S, H, D], contiguous (row (b, s, h) holds D values).
+ *   x_i8    int8 [B, H, S_pad, D] out, S_pad = sage_seq_pad(S); rows >= S
+ *           are written as zeros.
+ *   x_scale fp32 [B, H, S_pad/32] out; block t covers rows [32t, 32t+32) of
+ *           one (b, h); blocks past S get 0.
+ * Per block: amax = max |x| over its valid rows (a short last block uses
+ * only its valid rows); scale = fl32(amax/127); q = clamp(rint_even(
+ * fl32(x * fl32(127/amax))), -127, 127); amax = 0 (or a non-finite
+ * reciprocal) gives scale 0 and q = 0. Pointers 16-byte aligned.
+ */
+sage_status sage_quant_qk(const void* x, int64_t B, int64_t S, int64_t H, int64_t D,
+                          int8_t* x_i8, float* x_scale, void* stream);
+
+/*
+ * sage_quant_v - FP8 E4M3FN quantization of V per channel (issue #15014,
+ * problem statement: "V per channel").
+ *   v        bf16 [B, S, H, D], contiguous.
+ *   v_fp8_t  uint8 [B, H, D, S_pad] out: OCP E4M3FN codes, transposed (one
+ *            row of S_pad keys per channel). Within each group of 64 keys
+ *            starting at a multiple of 64, slot p holds key
+ *              kappa(p) = 32*u + 8*(r/4) + 4*g + (r%4),
+ *            where p = 32*g + 16*u + r, g in {0,1}, u in {0,1}, r in [0,16)
+ *            (the key order the fused kernel's PV operands use). Keys >= S
+ *            hold code 0.
+ *   v_scale  fp32 [B, H, D] out.
+ *   scratch  device memory of sage_quant_v_scratch_bytes(...) bytes.
+ * Per channel c of (b, h): amax = max over s < S of |v|; v_scale =
+ * fl32(amax/448); code = E4M3FN_rne(fl32(v * fl32(448/amax))); amax = 0
+ * gives scale 0 and code 0. 448 is the largest E4M3FN value.
+ */
+sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t D,
+                         uint8_t* v_fp8_t, float* v_scale, void* scratch, size_t scratch_bytes,
+                         void* stream);
+
+/*
+ * sage_attn_fwd - fused attention on quantized inputs (issue #15014,
+ * problem statement: INT8 QK^T and FP8 PV with FP32 accumulation).
+ * Inputs are the outputs of sage_quant_qk (Q and K) and sage_quant_v.
+ * out: bf16 [B, S, H, D] (the input layout), rows >= S are not written.
+ * Per query row i, over key tiles of sage_kv_tile() keys in key order:
+ *   A = q8 . k8^T (exact int32);  c = fl32(fl32(softmax_scale)*fl32(log2 e));
+ *   f = fl32(fl32(q_scale*k_scale)*c) per (query block, key block);
+ *   t = fl32(A*f); m = running max of t (keys >= S masked);
+ *   m2 = fl32(m - fl32(log2 448)); P' = 2^fl32(A*f - m2) (fused multiply-add,
+ *   hardware exp2), so P' = 448 * 2^(t - m) up to rounding;
+ *   l = sum of fp32 P' (rescaled by 2^(m2_old - m2) when the max moves);
+ *   p8 = E4M3FN(min(P', 448)); acc[c] = sum p8 * v8[c] (FP8 MFMA, fp32
+ *   accumulation, same rescaling); out = bf16_rne(acc * v_scale[c] / l).
+ */
+sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                          const float* k_scale, const uint8_t* v_fp8_t, const float* v_scale,
+                          int64_t B, int64_t S, int64_t H, int64_t D, float softmax_scale, void* out,
+                          void* stream);
+
+/*
+ * sage_attention - one call: sage_quant_qk(Q), sage_quant_qk(K),
+ * sage_quant_v(V) and sage_attn_fwd, with every intermediate inside the
+ * caller's workspace (>= sage_workspace_bytes(B, S, H, D) bytes, 256-byte
+ * aligned). This is the gfx1201_sage_attention(q, k, v, softmax_scale)
+ * operation of the issue's problem statement. q, k, v, out: bf16
+ * [B, S, H, D].
+ */
+sage_status sage_attention(const void* q, const void* k, const void* v, int64_t B, int64_t S,
+                           int64_t H, int64_t D, float softmax_scale, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * sage_debug_qk_scores - debug dump of the exact int32 scores A = q8 . k8^T
+ * of one (b, h), rows [r0, r0+nr) x keys [c0, c0+nc), computed by the same
+ * INT8 MFMA operand loading and instruction sequence as sage_attn_fwd.
+ *   scores  int32 [nr, nc] out, row-major.
+ * Windows must satisfy 0 <= r0, 0 < nr, r0+nr <= S_pad (same for keys).
+ */
+sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t B, int64_t S,
+                                 int64_t H, int64_t D, int64_t b, int64_t h, int64_t r0,
+                                 int64_t nr, int64_t c0, int64_t nc, int32_t* scores,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H */

@@ -1,0 +1,274 @@
+// C ABI of the quantized attention forward (declared in include/sage.h):
+// host-side validation, workspace layout and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdarg>
+#include <cstdlib>
+#include <cstring>
+
+#include "sage.h"
+#include "sage_attn.hpp"
+#include "sage_common.hpp"
+#include "sage_quant.hpp"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+thread_local char g_last_error[512] = "";
+
+sage_status fail(sage_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sage_status fail(sage_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+// Test hook: SAGE_TEST_FAIL_LAUNCH=1 makes every launching entry point
+// report SAGE_ERR_HIP after validation, without launching, so callers' error
+// paths can be exercised on any host.
+bool forced_launch_failure() {
+  const char* e = getenv("SAGE_TEST_FAIL_LAUNCH");
+  return e && e[0] == '1';
+}
+
+int64_t seq_pad(int64_t S) { return (S + sage::kSeqAlign - 1) / sage::kSeqAlign * sage::kSeqAlign; }
+
+sage_status check_shape(int64_t B, int64_t S, int64_t H, int64_t D) {
+  if (D != sage::kHeadDim) return fail(SAGE_ERR_UNSUPPORTED, "head dim %lld unsupported (only 128)", (long long)D);
+  if (B < 1 || S < 1 || H < 1) return fail(SAGE_ERR_SHAPE, "B, S, H must be >= 1 (got %lld, %lld, %lld)",
+                                           (long long)B, (long long)S, (long long)H);
+  // S_pad * B * H * D must stay well inside int64, and S inside int32
+  if (S > (int64_t)1 << 30 || B > (int64_t)1 << 20 || H > (int64_t)1 << 20)
+    return fail(SAGE_ERR_SHAPE, "sizes too large");
+  const double n = (double)B * (double)H * (double)seq_pad(S) * 128.0;
+  if (n >= 4.0e18) return fail(SAGE_ERR_SHAPE, "sizes overflow");
+  return SAGE_OK;
+}
+
+sage_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(SAGE_ERR_NULL, "%s is NULL", name);
+  if (((uintptr_t)p) & 15) return fail(SAGE_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return SAGE_OK;
+}
+
+#define SAGE_TRY(expr)                  \
+  do {                                  \
+    sage_status _s = (expr);            \
+    if (_s != SAGE_OK) return _s;       \
+  } while (0)
+
+sage_status launched(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SAGE_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return SAGE_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t v_nchunk(int64_t S) { return (S + sage::kVChunkRows - 1) / sage::kVChunkRows; }
+
+size_t v_scratch_bytes(int64_t B, int64_t S, int64_t H) {
+  // partial maxima [B*H, nchunk, 128] + reciprocals [B*H, 128]
+  return align256((size_t)(B * H * v_nchunk(S) * 128) * 4) + align256((size_t)(B * H * 128) * 4);
+}
+
+struct Workspace {
+  size_t q8, k8, v8, qs, ks, vs, scratch, total, scratch_bytes;
+};
+
+Workspace layout(int64_t B, int64_t S, int64_t H) {
+  Workspace w{};
+  const int64_t Sp = seq_pad(S);
+  const size_t qk = align256((size_t)(B * H * Sp * 128));
+  const size_t sc = align256((size_t)(B * H * (Sp / 32)) * 4);
+  w.q8 = 0;
+  w.k8 = w.q8 + qk;
+  w.v8 = w.k8 + qk;
+  w.qs = w.v8 + qk;
+  w.ks = w.qs + sc;
+  w.vs = w.ks + sc;
+  w.scratch = w.vs + align256((size_t)(B * H * 128) * 4);
+  w.scratch_bytes = v_scratch_bytes(B, S, H);
+  w.total = w.scratch + w.scratch_bytes;
+  return w;
+}
+
+sage_status quant_qk_impl(const void* x, int64_t B, int64_t S, int64_t H, int8_t* xq, float* xs,
+                          hipStream_t st) {
+  const int64_t Sp = seq_pad(S);
+  const int nbp = (int)(Sp / sage::kQBlock);
+  const int64_t total = B * H * nbp;
+  const int64_t grid = (total + 3) / 4;
+  if (grid > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
+  hipLaunchKernelGGL(sage::quant_qk_kernel, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)x,
+                     (int)S, (int)H, (int)Sp, nbp, total, xq, xs);
+  return launched("sage_quant_qk");
+}
+
+sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, uint8_t* vt, float* vs,
+                         void* scratch, hipStream_t st) {
+  const int64_t Sp = seq_pad(S);
+  const int nchunk = (int)v_nchunk(S);
+  const int64_t BH = B * H;
+  if (BH > 65535 * 1024LL) return fail(SAGE_ERR_SHAPE, "B*H too large");
+  float* partial = (float*)scratch;
+  float* vinv = (float*)((char*)scratch + align256((size_t)(BH * nchunk * 128) * 4));
+  // B*H goes in grid.y (limit 65535 on HIP): fold larger products into x.
+  if (BH > 65535) return fail(SAGE_ERR_SHAPE, "B*H above 65535 unsupported");
+  hipLaunchKernelGGL(sage::v_amax_partial_kernel, dim3(nchunk, (unsigned)BH), dim3(256), 0, st,
+                     (const uint16_t*)v, (int)S, (int)H, nchunk, partial);
+  SAGE_TRY(launched("sage_quant_v (amax)"));
+  hipLaunchKernelGGL(sage::v_scale_kernel, dim3((unsigned)BH), dim3(128), 0, st, (const float*)partial,
+                     nchunk, vs, vinv);
+  SAGE_TRY(launched("sage_quant_v (scale)"));
+  hipLaunchKernelGGL(sage::v_quant_kernel, dim3((unsigned)(Sp / 128), (unsigned)BH), dim3(256), 0, st,
+                     (const uint16_t*)v, (int)S, (int)H, (int)Sp, (const float*)vinv, vt);
+  return launched("sage_quant_v (quantize)");
+}
+
+sage_status attn_impl(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
+                      const uint8_t* vt, const float* vs, int64_t B, int64_t S, int64_t H,
+                      float softmax_scale, void* out, hipStream_t st) {
+  const int64_t Sp = seq_pad(S);
+  const int nqt = (int)((S + sage::kQueryTile - 1) / sage::kQueryTile);
+  const int64_t nwg = B * H * nqt;
+  if (nwg > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
+  const float c = (float)softmax_scale * (float)1.4426950408889634;  // fl32(fl32(scale) * fl32(log2 e))
+  const float log2_448 = (float)std::log2(448.0);
+  hipLaunchKernelGGL(sage::attn_fwd_kernel, dim3((unsigned)nwg), dim3(256), 0, st, q8, qs, k8, ks, vt, vs,
+                     (int)S, (int)H, (int)Sp, nqt, (int)nwg, c, log2_448, (uint16_t*)out);
+  return launched("sage_attn_fwd");
+}
+
+}  // namespace
+
+extern "C" {
+
+int sage_abi_version(void) { return kAbiVersion; }
+
+const char* sage_status_str(int s) {
+  switch (s) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_ERR_NULL: return "SAGE_ERR_NULL";
+    case SAGE_ERR_SHAPE: return "SAGE_ERR_SHAPE";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED";
+    case SAGE_ERR_ALIGN: return "SAGE_ERR_ALIGN";
+    case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE";
+    case SAGE_ERR_HIP: return "SAGE_ERR_HIP";
+    case SAGE_ERR_RANGE: return "SAGE_ERR_RANGE";
+    default: return "SAGE_ERR_UNKNOWN";
+  }
+}
+
+const char* sage_last_error(void) { return g_last_error; }
+
+int sage_kv_tile(void) { return sage::kKeyTile; }
+
+int64_t sage_seq_pad(int64_t S) { return S < 1 ? 0 : seq_pad(S); }
+
+size_t sage_quant_v_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
+  if (check_shape(B, S, H, D) != SAGE_OK) return 0;
+  return v_scratch_bytes(B, S, H);
+}
+
+size_t sage_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
+  if (check_shape(B, S, H, D) != SAGE_OK) return 0;
+  return layout(B, S, H).total;
+}
+
+sage_status sage_quant_qk(const void* x, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* x_i8,
+                          float* x_scale, void* stream) {
+  SAGE_TRY(check_shape(B, S, H, D));
+  SAGE_TRY(check_ptr(x, "x"));
+  SAGE_TRY(check_ptr(x_i8, "x_i8"));
+  SAGE_TRY(check_ptr(x_scale, "x_scale"));
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  return quant_qk_impl(x, B, S, H, x_i8, x_scale, (hipStream_t)stream);
+}
+
+sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t D, uint8_t* v_fp8_t,
+                         float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
+  SAGE_TRY(check_shape(B, S, H, D));
+  SAGE_TRY(check_ptr(v, "v"));
+  SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
+  SAGE_TRY(check_ptr(v_scale, "v_scale"));
+  SAGE_TRY(check_ptr(scratch, "scratch"));
+  if (scratch_bytes < v_scratch_bytes(B, S, H))
+    return fail(SAGE_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, v_scratch_bytes(B, S, H));
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  return quant_v_impl(v, B, S, H, v_fp8_t, v_scale, scratch, (hipStream_t)stream);
+}
+
+sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                          const uint8_t* v_fp8_t, const float* v_scale, int64_t B, int64_t S, int64_t H,
+                          int64_t D, float softmax_scale, void* out, void* stream) {
+  SAGE_TRY(check_shape(B, S, H, D));
+  SAGE_TRY(check_ptr(q_i8, "q_i8"));
+  SAGE_TRY(check_ptr(q_scale, "q_scale"));
+  SAGE_TRY(check_ptr(k_i8, "k_i8"));
+  SAGE_TRY(check_ptr(k_scale, "k_scale"));
+  SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
+  SAGE_TRY(check_ptr(v_scale, "v_scale"));
+  SAGE_TRY(check_ptr(out, "out"));
+  if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, H, softmax_scale, out,
+                   (hipStream_t)stream);
+}
+
+sage_status sage_attention(const void* q, const void* k, const void* v, int64_t B, int64_t S, int64_t H,
+                           int64_t D, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  SAGE_TRY(check_shape(B, S, H, D));
+  SAGE_TRY(check_ptr(q, "q"));
+  SAGE_TRY(check_ptr(k, "k"));
+  SAGE_TRY(check_ptr(v, "v"));
+  SAGE_TRY(check_ptr(out, "out"));
+  if (!workspace) return fail(SAGE_ERR_NULL, "workspace is NULL");
+  if (((uintptr_t)workspace) & 255) return fail(SAGE_ERR_ALIGN, "workspace is not 256-byte aligned");
+  const Workspace w = layout(B, S, H);
+  if (workspace_bytes < w.total)
+    return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
+  if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  char* ws = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  int8_t* q8 = (int8_t*)(ws + w.q8);
+  int8_t* k8 = (int8_t*)(ws + w.k8);
+  uint8_t* v8 = (uint8_t*)(ws + w.v8);
+  float* qs = (float*)(ws + w.qs);
+  float* ks = (float*)(ws + w.ks);
+  float* vs = (float*)(ws + w.vs);
+  SAGE_TRY(quant_qk_impl(q, B, S, H, q8, qs, st));
+  SAGE_TRY(quant_qk_impl(k, B, S, H, k8, ks, st));
+  SAGE_TRY(quant_v_impl(v, B, S, H, v8, vs, ws + w.scratch, st));
+  return attn_impl(q8, qs, k8, ks, v8, vs, B, S, H, softmax_scale, out, st);
+}
+
+sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t B, int64_t S, int64_t H,
+                                 int64_t D, int64_t b, int64_t h, int64_t r0, int64_t nr, int64_t c0,
+                                 int64_t nc, int32_t* scores, void* stream) {
+  SAGE_TRY(check_shape(B, S, H, D));
+  SAGE_TRY(check_ptr(q_i8, "q_i8"));
+  SAGE_TRY(check_ptr(k_i8, "k_i8"));
+  if (!scores) return fail(SAGE_ERR_NULL, "scores is NULL");
+  const int64_t Sp = seq_pad(S);
+  if (b < 0 || b >= B || h < 0 || h >= H) return fail(SAGE_ERR_RANGE, "(b, h) outside the tensor");
+  if (r0 < 0 || nr < 1 || r0 + nr > Sp || c0 < 0 || nc < 1 || c0 + nc > Sp)
+    return fail(SAGE_ERR_RANGE, "window outside [0, S_pad)");
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  const int64_t rA = r0 / 32 * 32, cA = c0 / 128 * 128;
+  const int64_t gy = (r0 + nr - rA + sage::kQueryTile - 1) / sage::kQueryTile;
+  const int64_t gx = (c0 + nc - cA + sage::kKeyTile - 1) / sage::kKeyTile;
+  if (gx > INT32_MAX || gy > 65535) return fail(SAGE_ERR_RANGE, "window too large");
+  hipLaunchKernelGGL(sage::debug_qk_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, (hipStream_t)stream,
+                     q_i8, k_i8, (int)Sp, b * H + h, (int)rA, (int)r0, (int)nr, (int)cA, (int)c0, (int)nc,
+                     scores);
+  return launched("sage_debug_qk_scores");
+}
+
+}  // extern "C"

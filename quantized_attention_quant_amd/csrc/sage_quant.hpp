@@ -1,0 +1,164 @@
+// Quantization pre-pass kernels: INT8 Q/K per 32-row block, FP8 V per channel.
+//
+// Source: diffusers issue #15014, "gfx1201 (RDNA4) SageAttention attention
+// backend: aiter package or Hub kernel?", problem statement (Q/K per 32-row
+// block, V per channel, INT8 QK^T and FP8 PV). Both passes are bound by HBM
+// bandwidth: each reads its bf16 input once (V twice: amax, then quantize)
+// and writes one byte per element.
+#pragma once
+
+#include "sage_common.hpp"
+
+namespace sage {
+
+// One wave per (b, h, 32-row block); 4 waves per workgroup.
+// Lane l covers columns [8 (l%16), +8) of rows 4 it + l/16, it = 0..7.
+__global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restrict__ x, int S, int H,
+                                                       int S_pad, int nbp, int64_t total_blocks,
+                                                       int8_t* __restrict__ xq,
+                                                       float* __restrict__ xscale) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + wave;
+  if (blk >= total_blocks) return;
+  const int t = (int)(blk % nbp);
+  const int64_t bh = blk / nbp;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const int col = (lane & 15) * 8;
+  const int r0 = t * kQBlock;
+
+  float v[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = r0 + it * 4 + (lane >> 4);
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row < S) w = *(const uint4*)(x + (((b * S + row) * H + h) * kHeadDim + col));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[it][2 * j] = bf16_to_f32(ws[j] & 0xFFFFu);
+      v[it][2 * j + 1] = bf16_to_f32(ws[j] >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(v[it][2 * j]), fabsf(v[it][2 * j + 1])));
+    }
+  }
+  amax = wave_max(amax);
+  float scale = 0.0f, inv = 0.0f;
+  if (amax > 0.0f) {
+    inv = __fdiv_rn(127.0f, amax);
+    scale = __fdiv_rn(amax, 127.0f);
+    if (!isfinite(inv)) { inv = 0.0f; scale = 0.0f; }
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = r0 + it * 4 + (lane >> 4);
+    uint32_t packed[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float y = __builtin_rintf(v[it][j] * inv);
+      y = fminf(fmaxf(y, -127.0f), 127.0f);
+      const uint32_t byte = (uint32_t)((int)y) & 0xFFu;
+      packed[j >> 2] |= byte << (8 * (j & 3));
+    }
+    *(uint2*)(xq + ((bh * S_pad + row) * kHeadDim + col)) = make_uint2(packed[0], packed[1]);
+  }
+  if (lane == 0) xscale[bh * nbp + t] = scale;
+}
+
+// Partial per-channel amax of |V| over a chunk of kVChunkRows rows.
+// grid (nchunk, B*H), 256 threads: thread t covers channels [8 (t%16), +8)
+// of rows t/16 + 16 i.
+__global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __restrict__ v, int S,
+                                                             int H, int nchunk,
+                                                             float* __restrict__ partial) {
+  __shared__ float red[16][kHeadDim];
+  const int chunk = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const int cg = threadIdx.x & 15, ro = threadIdx.x >> 4;
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int rbeg = chunk * kVChunkRows;
+  const int rend = min(S, rbeg + kVChunkRows);
+  for (int row = rbeg + ro; row < rend; row += 16) {
+    const uint4 w = *(const uint4*)(v + (((b * S + row) * H + h) * kHeadDim + cg * 8));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[2 * j] = fmaxf(m[2 * j], fabsf(bf16_to_f32(ws[j] & 0xFFFFu)));
+      m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(bf16_to_f32(ws[j] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[ro][cg * 8 + j] = m[j];
+  __syncthreads();
+  if (threadIdx.x < kHeadDim) {
+    float r = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r = fmaxf(r, red[i][threadIdx.x]);
+    partial[(bh * nchunk + chunk) * kHeadDim + threadIdx.x] = r;
+  }
+}
+
+// Per-channel amax over all chunks -> v_scale and the fp32 reciprocal.
+// grid B*H, 128 threads (one per channel).
+__global__ __launch_bounds__(128) void v_scale_kernel(const float* __restrict__ partial, int nchunk,
+                                                      float* __restrict__ vscale,
+                                                      float* __restrict__ vinv) {
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x;
+  float amax = 0.0f;
+  for (int i = 0; i < nchunk; ++i) amax = fmaxf(amax, partial[(bh * nchunk + i) * kHeadDim + c]);
+  float scale = 0.0f, inv = 0.0f;
+  if (amax > 0.0f) {
+    inv = __fdiv_rn(448.0f, amax);
+    scale = __fdiv_rn(amax, 448.0f);
+    if (!isfinite(inv)) { inv = 0.0f; scale = 0.0f; }
+  }
+  vscale[bh * kHeadDim + c] = scale;
+  vinv[bh * kHeadDim + c] = inv;
+}
+
+// Quantize 128 keys x 128 channels of V to E4M3FN and write them transposed
+// ([channel][key]) with keys permuted inside each 64-key group.
+// grid (S_pad/128, B*H), 256 threads.
+__global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict__ v, int S, int H,
+                                                      int S_pad, const float* __restrict__ vinv,
+                                                      uint8_t* __restrict__ vt) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim][128 + 16];
+  const int k0 = blockIdx.x * 128;
+  const int64_t bh = blockIdx.y;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const int cg = threadIdx.x & 15, ro = threadIdx.x >> 4;
+  float inv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) inv[j] = vinv[bh * kHeadDim + cg * 8 + j];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int kk = ro + 16 * i;  // key within the 128-key tile
+    const int row = k0 + kk;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row < S) w = *(const uint4*)(v + (((b * S + row) * H + h) * kHeadDim + cg * 8));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const int slot = (kk & ~(kVGroup - 1)) | vslot_of_key(kk & (kVGroup - 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float y0 = bf16_to_f32(ws[j] & 0xFFFFu) * inv[2 * j];
+      float y1 = bf16_to_f32(ws[j] >> 16) * inv[2 * j + 1];
+      y0 = fminf(fmaxf(y0, -448.0f), 448.0f);
+      y1 = fminf(fmaxf(y1, -448.0f), 448.0f);
+      const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      tile[cg * 8 + 2 * j][slot] = (uint8_t)(pk & 0xFFu);
+      tile[cg * 8 + 2 * j + 1][slot] = (uint8_t)((pk >> 8) & 0xFFu);
+    }
+  }
+  __syncthreads();
+  const int c = threadIdx.x >> 1, half = threadIdx.x & 1;
+  uint8_t* dst = vt + (bh * kHeadDim + c) * (int64_t)S_pad + k0 + 64 * half;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *(uint4*)(dst + 16 * q) = *(const uint4*)(&tile[c][64 * half + 16 * q]);
+}
+
+}  // namespace sage

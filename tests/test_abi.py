@@ -1,0 +1,121 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point include/sage.h declares, and rejects bad arguments before any launch.
+
+Only validation paths and pure queries are called here; fake device pointers
+are never dereferenced because every call below returns before launching.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_attention_quant_amd as sage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP, ERR_RANGE = range(8)
+FAKE = 0x100000          # aligned, never dereferenced
+MISALIGNED = 0x100008
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attention", "sage_debug_qk_scores",
+              "sage_workspace_bytes", "sage_kv_tile", "sage_seq_pad"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = sage.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", sage.library_path], capture_output=True, text=True)
+    if out.returncode == 0:
+        exported = set(re.findall(r"\bT (sage_\w+)", out.stdout))
+        assert set(_declared()) <= exported
+
+
+def test_queries():
+    assert sage.sage_abi_version() == 1
+    bn = sage.sage_kv_tile()
+    assert bn % 32 == 0 and bn >= 32
+    for S, Sp in ((1, 256), (256, 256), (257, 512), (75600, 75776), (16384, 16384)):
+        assert sage.sage_seq_pad(S) == Sp
+    # workspace: three one-byte-per-element tensors plus small scales/scratch
+    for B, S, H in ((1, 256, 2), (1, 16384, 24), (2, 75600, 40)):
+        Sp = sage.sage_seq_pad(S)
+        ws = sage.sage_workspace_bytes(B, S, H, 128)
+        base = 3 * B * H * Sp * 128
+        assert base <= ws <= base * 1.02 + 65536
+    assert sage.sage_workspace_bytes(1, 256, 2, 64) == 0
+    assert sage.sage_workspace_bytes(0, 256, 2, 128) == 0
+    assert sage.lib().sage_status_str(ERR_WS) == b"SAGE_ERR_WORKSPACE"
+
+
+def _call(name, *args):
+    fn = getattr(sage.lib(), name)
+    return fn(*args)
+
+
+def test_validation_codes():
+    p = ctypes.c_void_p
+    f, m = p(FAKE), p(MISALIGNED)
+    z = p(0)
+    # head dim, sizes
+    assert _call("sage_quant_qk", f, 1, 256, 2, 64, f, f, z) == ERR_UNSUP
+    assert _call("sage_quant_qk", f, 0, 256, 2, 128, f, f, z) == ERR_SHAPE
+    assert _call("sage_quant_qk", f, 1, -5, 2, 128, f, f, z) == ERR_SHAPE
+    assert _call("sage_quant_qk", f, 1, 1 << 40, 2, 128, f, f, z) == ERR_SHAPE
+    # pointers
+    assert _call("sage_quant_qk", z, 1, 256, 2, 128, f, f, z) == ERR_NULL
+    assert _call("sage_quant_qk", m, 1, 256, 2, 128, f, f, z) == ERR_ALIGN
+    assert b"not 16-byte aligned" in sage.lib().sage_last_error()
+    # scratch / workspace sizes
+    need = sage.sage_quant_v_scratch_bytes(1, 256, 2)
+    assert _call("sage_quant_v", f, 1, 256, 2, 128, f, f, f, need - 1, z) == ERR_WS
+    ws = sage.sage_workspace_bytes(1, 256, 2)
+    assert _call("sage_attention", f, f, f, 1, 256, 2, 128, ctypes.c_float(0.1), f, f, ws - 1, z) == ERR_WS
+    assert _call("sage_attention", f, f, f, 1, 256, 2, 128, ctypes.c_float(0.1), f, p(FAKE + 16), ws, z) == ERR_ALIGN
+    assert _call("sage_attention", f, f, f, 1, 256, 2, 128, ctypes.c_float(float("nan")), f, f, ws, z) == ERR_SHAPE
+    assert _call("sage_attn_fwd", f, f, f, f, f, z, 1, 256, 2, 128, ctypes.c_float(0.1), f, z) == ERR_NULL
+    # debug window
+    assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 128, 0, 0, 0, 256, 0, 257, f, z) == ERR_RANGE
+    assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 128, 0, 2, 0, 1, 0, 1, f, z) == ERR_RANGE
+    assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 128, 0, 0, 0, 0, 0, 1, f, z) == ERR_RANGE
+
+
+def test_forced_launch_failure_hook(monkeypatch):
+    monkeypatch.setenv("SAGE_TEST_FAIL_LAUNCH", "1")
+    p = ctypes.c_void_p
+    f, z = p(FAKE), p(0)
+    assert _call("sage_quant_qk", f, 1, 256, 2, 128, f, f, z) == ERR_HIP
+    ws = sage.sage_workspace_bytes(1, 256, 2)
+    assert _call("sage_attention", f, f, f, 1, 256, 2, 128, ctypes.c_float(0.1), f, f, ws, z) == ERR_HIP
+    assert b"forced" in sage.lib().sage_last_error()
+    # validation still runs first
+    assert _call("sage_quant_qk", f, 1, 256, 2, 64, f, f, z) == ERR_UNSUP
+
+
+def test_binding_raises_on_missing_library(monkeypatch):
+    monkeypatch.setattr(sage, "_lib", None)
+    monkeypatch.setattr(sage, "library_path", "/nonexistent/libsage.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        sage.lib()
+
+
+def test_binding_rejects_non_bf16_inputs():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((1, 32, 1, 128), dtype=torch.float32)
+    with pytest.raises((ValueError, TypeError)):
+        sage.sage_quant_qk(x)
+    with pytest.raises(ValueError):
+        sage.sage_attention(x, x, x)

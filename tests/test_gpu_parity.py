@@ -1,0 +1,342 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Gates:
+* INT8 Q/K codes and scales, FP8 V codes and scales, and the int32 scores
+  (debug dump through the fused kernel's MFMA path) are bit-exact;
+* the output satisfies max|O_gpu - O_oracle| <= 1e-2 * max|O_oracle| and
+  cosine >= 0.9999 on the compared rows, and cosine >= 0.99 against exact
+  fp64 attention.
+Small sizes are compared in full; the full-size configurations run in the
+launch configuration the benchmark times and are compared on sampled query
+blocks (first, last and random blocks of sampled heads) that the oracle
+computes row by row.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+sage = pytest.importorskip("quantized_attention_quant_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(DEV)
+
+
+def kappa(p):
+    """Key of slot p in a 64-key group of the V^T layout (include/sage.h)."""
+    g, u, r = p // 32, (p // 16) % 2, p % 16
+    return 32 * u + 8 * (r // 4) + 4 * g + (r % 4)
+
+
+def unpermute_vt(vt, S):
+    """[B,H,D,S_pad] permuted -> [B,H,S,D] natural key order."""
+    B, H, D, Sp = vt.shape
+    perm = np.empty(Sp, dtype=np.int64)
+    for w in range(Sp // 64):
+        for p in range(64):
+            perm[w * 64 + kappa(p)] = w * 64 + p
+    nat = vt[:, :, :, perm]
+    return np.transpose(nat, (0, 1, 3, 2))[:, :, :S]
+
+
+def cosine(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def gate(got, ref, exact=None, label=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), label
+    err = np.max(np.abs(got - ref))
+    c = cosine(got, ref)
+    _say(f"  {label}: max|err| {err:.4g} (bound {1e-2 * np.max(np.abs(ref)):.4g}), cosine {c:.7f}"
+         + (f", cos vs fp64 {cosine(got, exact):.5f}" if exact is not None else ""))
+    assert err <= 1e-2 * np.max(np.abs(ref)), label
+    assert c >= 0.9999, label
+    if exact is not None:
+        assert cosine(got, exact) >= 0.99, label
+
+
+def exact_rows(q, k, v, b, h, rows, scale):
+    qh = q[b, rows, h, :].astype(np.float64)
+    s = qh @ k[b, :, h, :].astype(np.float64).T * scale
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ v[b, :, h, :].astype(np.float64)) / p.sum(axis=1, keepdims=True)
+
+
+def oracle_rows(q, k, v, b, h, rows, scale, bn):
+    sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1, :])  # noqa: E731
+    q8, qs = oracle.quant_qk(sl(q))
+    k8, ks = oracle.quant_qk(sl(k))
+    v8, vs = oracle.quant_v(sl(v))
+    return oracle.attention_head(q8[0, 0], qs[0, 0], k8[0, 0], ks[0, 0], v8[0, 0], vs[0, 0], scale, bn,
+                                 rows=rows)
+
+
+def run_split(q, k, v, scale):
+    """Quantize and attend through the split entry points; returns host arrays."""
+    B, S, H, D = q.shape
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    q8, qs = sage.sage_quant_qk(qd)
+    k8, ks = sage.sage_quant_qk(kd)
+    v8, vs = sage.sage_quant_v(vd)
+    out = torch.full((B, S, H, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    sage.sage_attn_fwd(q8, qs, k8, ks, v8, vs, B, S, H, D, scale, out=out)
+    torch.cuda.synchronize()
+    return dict(q8=q8, qs=qs, k8=k8, ks=ks, v8=v8, vs=vs, out=out)
+
+
+# --------------------------------------------------------------------------
+# bit-exact quantization
+
+@pytest.mark.parametrize("S", [1, 31, 33, 200, 256, 300])
+def test_quant_qk_bit_exact(S):
+    _say(f"quant_qk S={S}")
+    x = workloads.generate(3, S=S, H=3, seed=200 + S)[0]
+    B, _, H, D = x.shape
+    Sp = sage.sage_seq_pad(S)
+    xq = torch.full((B, H, Sp, D), 77, dtype=torch.int8, device=DEV)          # poison
+    xs = torch.full((B, H, Sp // 32), float("nan"), dtype=torch.float32, device=DEV)
+    sage.sage_quant_qk(to_dev(x), xq, xs)
+    torch.cuda.synchronize()
+    q8, qs = oracle.quant_qk(x)
+    g8, gs = xq.cpu().numpy(), xs.cpu().numpy()
+    assert np.array_equal(g8[:, :, :S], q8)
+    assert np.all(g8[:, :, S:] == 0)
+    nb = (S + 31) // 32
+    assert np.array_equal(gs[:, :, :nb].view(np.uint32), qs.view(np.uint32))
+    assert np.all(gs[:, :, nb:] == 0)
+
+
+@pytest.mark.parametrize("idx,S,H", [(1, 256, 2), (2, 4096, 4), (3, 1000, 3), (5, 333, 2)])
+def test_quant_v_bit_exact(idx, S, H):
+    _say(f"quant_v config {idx} S={S} H={H}")
+    v = workloads.generate(idx, S=S, H=H, B=1)[2]
+    B, _, _, D = v.shape
+    Sp = sage.sage_seq_pad(S)
+    vt = torch.full((B, H, D, Sp), 0x7F, dtype=torch.uint8, device=DEV)     # poison (NaN code)
+    vs = torch.full((B, H, D), float("nan"), dtype=torch.float32, device=DEV)
+    sage.sage_quant_v(to_dev(v), vt, vs)
+    torch.cuda.synchronize()
+    v8, vsr = oracle.quant_v(v)
+    gt = vt.cpu().numpy()
+    assert np.array_equal(unpermute_vt(gt, S), v8)
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), vsr.view(np.uint32))
+    tail = unpermute_vt(gt, Sp)[:, :, S:]
+    assert np.all(tail == 0)
+
+
+def test_quant_edge_values():
+    _say("quant edge values")
+    x = workloads.generate_custom((1, 96, 2, 128), seed=7)
+    x[0, 32:64, 0] = 0.0                       # all-zero Q/K block
+    x[0, 64:96, 1] = np.float32(1e-39)         # reciprocal overflows: zero rule
+    x[0, 0, 0, 0] = 3.0e38                     # huge bf16 value
+    x[0, 5, 1, :4] = [0.5, 1.5, -2.5, 126.5]
+    x = workloads.bf16_round(x)
+    xq, xs = sage.sage_quant_qk(to_dev(x))
+    torch.cuda.synchronize()
+    q8, qs = oracle.quant_qk(x)
+    assert np.array_equal(xq.cpu().numpy()[:, :, :96], q8)
+    assert np.array_equal(xs.cpu().numpy()[:, :, :3].view(np.uint32), qs.view(np.uint32))
+    v = x.copy()
+    v[..., 7] = 0.0                            # zero channel
+    vt, vs = sage.sage_quant_v(to_dev(v))
+    torch.cuda.synchronize()
+    v8, vsr = oracle.quant_v(v)
+    assert np.array_equal(unpermute_vt(vt.cpu().numpy(), 96), v8)
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), vsr.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# bit-exact int32 scores through the fused kernel's MFMA path
+
+def test_debug_scores_full_config1():
+    _say("debug scores config 1")
+    q, k, _ = workloads.generate(1)
+    B, S, H, D = q.shape
+    q8, qs = sage.sage_quant_qk(to_dev(q))
+    k8, ks = sage.sage_quant_qk(to_dev(k))
+    oq, _ = oracle.quant_qk(q)
+    ok, _ = oracle.quant_qk(k)
+    for b in range(B):
+        for h in range(H):
+            got = sage.sage_debug_qk_scores(q8, k8, B, S, H, b, h, 0, S, 0, S)
+            torch.cuda.synchronize()
+            assert np.array_equal(got.cpu().numpy(), oracle.qk_scores(oq[b, h], ok[b, h]))
+
+
+@pytest.mark.parametrize("r0,nr,c0,nc", [(0, 1, 0, 1), (5, 70, 130, 300), (100, 250, 0, 512), (480, 32, 470, 42)])
+def test_debug_scores_windows(r0, nr, c0, nc):
+    _say(f"debug scores window {r0},{nr},{c0},{nc}")
+    q, k, _ = workloads.generate(2, S=500, H=3, seed=300)
+    B, S, H, D = q.shape
+    q8, _ = sage.sage_quant_qk(to_dev(q))
+    k8, _ = sage.sage_quant_qk(to_dev(k))
+    oq, _ = oracle.quant_qk(q)
+    ok, _ = oracle.quant_qk(k)
+    Sp = sage.sage_seq_pad(S)
+    pad = lambda a: np.concatenate([a, np.zeros((Sp - S, D), a.dtype)])  # noqa: E731
+    got = sage.sage_debug_qk_scores(q8, k8, B, S, H, 0, 2, r0, nr, c0, nc)
+    torch.cuda.synchronize()
+    ref = oracle.qk_scores(pad(oq[0, 2]), pad(ok[0, 2]))[r0:r0 + nr, c0:c0 + nc]
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_debug_scores_extreme_codes():
+    """|A| up to 128*127^2: int32 accumulation with no overflow or rounding."""
+    _say("debug scores extreme")
+    S = 64
+    x = np.zeros((1, S, 1, 128), np.float32)
+    x[0, 0] = 1.0
+    x[0, 1] = -1.0
+    x[0, 2:, 0] = workloads.generate_custom((S - 2, 128), seed=3, kind="uniform")
+    q8, _ = sage.sage_quant_qk(to_dev(x))
+    got = sage.sage_debug_qk_scores(q8, q8, 1, S, 1, 0, 0, 0, S, 0, S)
+    torch.cuda.synchronize()
+    oq, _ = oracle.quant_qk(x)
+    ref = oracle.qk_scores(oq[0, 0], oq[0, 0])
+    assert ref[0, 0] == 128 * 127 * 127 and ref[0, 1] == -128 * 127 * 127
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+# --------------------------------------------------------------------------
+# attention output
+
+@pytest.mark.parametrize("S,H,B", [(1, 1, 1), (32, 1, 1), (33, 2, 1), (127, 1, 1), (128, 1, 1), (129, 2, 1),
+                                   (200, 2, 2), (256, 2, 1), (600, 3, 1)])
+@pytest.mark.parametrize("recipe", [1, 3])
+def test_attention_small_full_compare(S, H, B, recipe):
+    _say(f"attention S={S} H={H} B={B} recipe {recipe}")
+    q, k, v = workloads.generate(recipe, S=S, H=H, B=B, seed=400 + S)
+    scale = 1.0 / math.sqrt(128)
+    r = run_split(q, k, v, scale)
+    got = r["out"].float().cpu().numpy()
+    ref = oracle.sage_attention(q, k, v, scale, sage.sage_kv_tile())
+    # the fp64 gate applies to the N(0,1) recipe; with the outlier recipe at a
+    # few dozen rows one x8 row dominates its block's scale and the method
+    # itself (the oracle too) drifts further from exact attention
+    exact = oracle.exact_attention_fp64(q, k, v, scale) if recipe == 1 else None
+    gate(got, ref, exact, f"S={S} recipe {recipe}")
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_attention_config_full_compare(idx):
+    cfg = workloads.config(idx)
+    _say(f"attention config {idx} ({cfg.name}), full compare")
+    q, k, v = workloads.generate(idx)
+    S = cfg.S
+    heads = [(0, h) for h in range(cfg.H)] if idx == 1 else [(0, 0), (0, 11), (0, 23)]
+    r = run_split(q, k, v, cfg.softmax_scale)
+    got = r["out"].float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    rows = np.arange(S)
+    for b, h in heads:
+        ref = oracle_rows(q, k, v, b, h, rows, cfg.softmax_scale, sage.sage_kv_tile())
+        ex = exact_rows(q, k, v, b, h, rows, cfg.softmax_scale) if S <= 4096 else None
+        gate(got[b, :, h, :], ref, ex, f"config {idx} head {h}")
+
+
+def _sample_rows(S, rng, nrand=2):
+    nb = (S + 31) // 32
+    blocks = sorted(set([0, nb - 1] + list(rng.choice(nb, nrand, replace=False))))
+    rows = np.concatenate([np.arange(32 * t, min(S, 32 * t + 32)) for t in blocks])
+    return rows
+
+
+@pytest.mark.parametrize("idx", [3, 4, 5])
+def test_attention_full_size_sampled(idx):
+    cfg = workloads.config(idx)
+    _say(f"attention config {idx} ({cfg.name}), sampled compare; generating inputs")
+    q, k, v = workloads.generate(idx, chunk_elems=1 << 26)
+    rng = np.random.default_rng(idx)
+    _say("  running the GPU path (one-shot sage_attention)")
+    out = sage.sage_attention(to_dev(q), to_dev(k), to_dev(v), cfg.softmax_scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy() if idx != 5 else None
+    pairs = [(0, 0), (cfg.B - 1, cfg.H - 1), (int(rng.integers(cfg.B)), int(rng.integers(cfg.H)))]
+    for b, h in pairs:
+        rows = _sample_rows(cfg.S, rng)
+        g = got[b, rows, h, :] if got is not None else out[b, torch.as_tensor(rows, device=DEV), h, :].float().cpu().numpy()
+        ref = oracle_rows(q, k, v, b, h, rows, cfg.softmax_scale, sage.sage_kv_tile())
+        ex = exact_rows(q, k, v, b, h, rows, cfg.softmax_scale)
+        gate(g, ref, ex, f"config {idx} (b,h)=({b},{h}) rows={len(rows)}")
+    if got is not None:
+        assert np.all(np.isfinite(got))
+    else:
+        assert bool(torch.isfinite(out).all())
+
+
+def test_one_shot_equals_split_and_is_deterministic():
+    _say("one-shot vs split, determinism")
+    q, k, v = workloads.generate(2, S=1000, H=4, seed=500)
+    scale = 1.0 / math.sqrt(128)
+    r = run_split(q, k, v, scale)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o1 = sage.sage_attention(qd, kd, vd, scale)
+    o2 = sage.sage_attention(qd, kd, vd, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), r["out"].view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_invariances_on_gpu():
+    _say("invariances")
+    q, k, v = workloads.generate(3, S=384, H=2, seed=600)
+    scale = 1.0 / math.sqrt(128)
+    base = run_split(q, k, v, scale)["out"].float().cpu().numpy()
+    perm = np.arange(384)
+    perm[64:96] = 64 + np.random.default_rng(0).permutation(32)
+    o_q = run_split(q[:, perm], k, v, scale)["out"].float().cpu().numpy()
+    assert np.array_equal(o_q, base[:, perm])
+    o_v = run_split(q, k, v * np.float32(4.0), scale)["out"].float().cpu().numpy()
+    assert np.array_equal(o_v, base * np.float32(4.0))
+    o_s = run_split(q * np.float32(2.0), k, v, scale / 2.0)["out"].float().cpu().numpy()
+    assert np.array_equal(o_s, base)
+
+
+def test_closed_forms_on_gpu():
+    _say("closed forms")
+    q, k, v = workloads.generate(1, S=300, H=1, seed=700)
+    scale = 1.0 / math.sqrt(128)
+    z = np.zeros_like(q)
+    o = run_split(q, k, z, scale)["out"].float().cpu().numpy()
+    assert np.all(o == 0)
+    o = run_split(q, z, v, scale)["out"].float().cpu().numpy()
+    ref = oracle.sage_attention(q, z, v, scale, sage.sage_kv_tile())
+    gate(o, ref, None, "K = 0")
+    o = run_split(z, k, v, scale)["out"].float().cpu().numpy()
+    ref = oracle.sage_attention(z, k, v, scale, sage.sage_kv_tile())
+    gate(o, ref, None, "Q = 0")
+
+
+def test_huge_scores_saturate_like_the_oracle():
+    """Scores above 2^19 in log2 units take the clamped P path."""
+    _say("huge scores")
+    rng = np.random.default_rng(5)
+    S = 256
+    q = workloads.bf16_round(np.sign(rng.standard_normal((1, S, 1, 128))).astype(np.float32) * 300.0)
+    k = q.copy()                      # the diagonal scores reach ~1.5e6 in log2 units
+    v = workloads.generate_custom((1, S, 1, 128), seed=6)
+    scale = 1.0 / math.sqrt(128)
+    got = run_split(q, k, v, scale)["out"].float().cpu().numpy()
+    ref = oracle.sage_attention(q, k, v, scale, sage.sage_kv_tile())
+    gate(got, ref, None, "huge scores")
