@@ -69,14 +69,151 @@ __device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ lds_k, const
 
 __device__ __forceinline__ int key_of(int u, int r, int g) { return 32 * u + 8 * (r >> 2) + 4 * g + (r & 3); }
 
+// Asynchronous copy of one 128-row x 128-byte tile into swizzled LDS with
+// global_load_lds_dwordx4: each wave instruction writes 1 KB (8 rows)
+// contiguously, lane l at +16 l, so the swizzle is applied by choosing each
+// lane's source chunk. kWaves waves split the 16 row groups.
+template <int kWaves>
+__device__ __forceinline__ void stage_tile_async(uint8_t* lds, const uint8_t* __restrict__ src, int64_t row_stride,
+                                                 int wave, int lane) {
+  const int rr = lane >> 3, cp = lane & 7;
+#pragma unroll
+  for (int i = 0; i < 16 / kWaves; ++i) {
+    const int grp = wave + kWaves * i;
+    const int row = 8 * grp + rr;
+    const uint8_t* g = src + row * row_stride + ((cp ^ rr) << 4);
+    __builtin_amdgcn_global_load_lds((const void*)g,
+                                     (__attribute__((address_space(3))) void*)(lds + grp * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ int imax3(int a, int b, int c) { return max(max(a, b), c); }
+
+// Largest of the 16 scores a lane holds for one sub-tile.
+__device__ __forceinline__ int max16(const v16i& s) {
+  int a = imax3(s[0], s[1], s[2]);
+  int b = imax3(s[3], s[4], s[5]);
+  a = imax3(a, s[6], s[7]);
+  b = imax3(b, s[8], s[9]);
+  a = imax3(a, s[10], s[11]);
+  b = imax3(b, s[12], s[13]);
+  a = imax3(a, s[14], s[15]);
+  return max(a, b);
+}
+
+// max / sum of a value over lanes l and l^32 (the two halves hold the same
+// query rows), with one v_permlane32_swap.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// P' = 2^(A f - m2) for the 64 scores of a lane, their fp32 sum, and the
+// E4M3FN codes packed in the FP8 MFMA B-operand order (byte 16 (u%2) + r of
+// pop[u/2] holds sub-tile u, register r). kClamp: saturate before the
+// conversion (the hardware conversion gives NaN above 464). kTail: keys at
+// or past `nvalid` get P' = 0.
+template <bool kClamp, bool kTail>
+__device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], float m2, int nvalid, int g,
+                                           v8i pop[2]) {
+  float lsum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * j + e;
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[u][r], f[u], -m2));
+        if (kTail && key_of(u, r, g) >= nvalid) pe = 0.0f;
+        lsum += pe;
+        p[e] = kClamp ? fminf(pe, 448.0f) : pe;
+      }
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+      pop[u >> 1][4 * (u & 1) + j] = wd;
+    }
+  }
+  return lsum;
+}
+
+struct RowState {
+  float m, m2, l;
+};
+
+// One key tile for one wave: QK^T, online softmax, PV.
+template <bool kTail>
+__device__ __forceinline__ void attn_tile(const uint8_t* lk, const uint8_t* lv, const v4i qf[4], float qs,
+                                          const float* __restrict__ ks4, float c, float log2_448, int nvalid,
+                                          int li, int g, RowState& st, v16f o[4]) {
+  v16i s[4];
+  qk_tile(lk, qf, li, g, s);
+  float f[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) f[u] = (qs * ks4[u]) * c;
+
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (kTail) {
+      if (32 * u >= nvalid) continue;
+      v16i sm = s[u];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key_of(u, r, g) >= nvalid) sm[r] = INT32_MIN;
+      tmax = fmaxf(tmax, (float)max16(sm) * f[u]);
+    } else {
+      tmax = fmaxf(tmax, (float)max16(s[u]) * f[u]);
+    }
+  }
+  tmax = pair_max(tmax);
+  const float m_new = fmaxf(st.m, tmax);
+  const float m2_new = m_new - log2_448;
+  const float alpha = __builtin_amdgcn_exp2f(st.m2 - m2_new);
+  v8i pop[2];
+  float lsum;
+  // Scores beyond 2^19 (log2 units) make the fp32 spacing of m coarse
+  // enough for P' to pass 464; that rare case takes the clamped variant.
+  if (__builtin_expect(__ballot(m_new > 524288.0f) != 0, 0))
+    lsum = softmax_p<true, kTail>(s, f, m2_new, nvalid, g, pop);
+  else
+    lsum = softmax_p<false, kTail>(s, f, m2_new, nvalid, g, pop);
+  st.l = st.l * alpha + lsum;
+  if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) o[cb] *= alpha;
+  }
+  st.m = m_new;
+  st.m2 = m2_new;
+
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int row = 32 * cb + li;
+      const v4i lo = *(const v4i*)(lv + swz(row, 4 * w + 2 * g));
+      const v4i hi = *(const v4i*)(lv + swz(row, 4 * w + 2 * g + 1));
+      const v8i vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop[w], o[cb], 0, 0, 0, 0, 0, 0);
+    }
+  }
+}
+
+constexpr int kAttnWaves = kQueryTile / 32;
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qscale,
                      const int8_t* __restrict__ k8, const float* __restrict__ kscale,
                      const uint8_t* __restrict__ v8t, const float* __restrict__ vscale, int S, int H,
                      int S_pad, int nqt, int num_wg, float c, float log2_448,
                      uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kKeyTile * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[kHeadDim * kKeyTile];
+  // two stages of (K tile, V^T tile), 16 KB each
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kKeyTile * 128];
 
   const int wg = xcd_remap(blockIdx.x, num_wg);
   const int qt = wg % nqt;
@@ -86,100 +223,48 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   const int q0 = qt * kQueryTile + wave * 32;
   const int nbp = S_pad / kQBlock;
 
+  const uint8_t* kbase = (const uint8_t*)k8 + bh * S_pad * kHeadDim;
+  const uint8_t* vbase = v8t + bh * kHeadDim * (int64_t)S_pad;
+  const float* ksb = kscale + bh * nbp;
+  const int ntiles = (S + kKeyTile - 1) / kKeyTile;
+  const int nfull = S / kKeyTile;   // tiles with no masked key
+
+  stage_tile_async<kAttnWaves>(lds[0][0], kbase, kHeadDim, wave, lane);
+  stage_tile_async<kAttnWaves>(lds[0][1], vbase, S_pad, wave, lane);
+
   v4i qf[4];
   load_q_frag(q8 + ((bh * S_pad + q0 + li) * kHeadDim + 64 * g), qf);
   const float qs = qscale[bh * nbp + q0 / kQBlock];
 
-  const uint8_t* kbase = (const uint8_t*)k8 + bh * S_pad * kHeadDim;
-  const uint8_t* vbase = v8t + bh * kHeadDim * (int64_t)S_pad;
-  const float* ksb = kscale + bh * nbp;
-
-  float m = -INFINITY, m2 = -INFINITY, l = 0.0f;
+  RowState st{-INFINITY, -INFINITY, 0.0f};
   v16f o[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) o[cb] = (v16f){0};
 
-  const int ntiles = (S + kKeyTile - 1) / kKeyTile;
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // Full tiles: tile kt+1 streams into the other LDS stage while tile kt is
+  // computed; one barrier per tile.
+  for (int kt = 0; kt < nfull; ++kt) {
     const int k0 = kt * kKeyTile;
+    const int buf = kt & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    stage_tile(lds_k, kbase + (int64_t)k0 * kHeadDim, kHeadDim, tid);
-    stage_tile(lds_v, vbase + k0, S_pad, tid);
+    if (kt + 1 < ntiles) {
+      stage_tile_async<kAttnWaves>(lds[buf ^ 1][0], kbase + (int64_t)(k0 + kKeyTile) * kHeadDim, kHeadDim, wave, lane);
+      stage_tile_async<kAttnWaves>(lds[buf ^ 1][1], vbase + k0 + kKeyTile, S_pad, wave, lane);
+    }
+    attn_tile<false>(lds[buf][0], lds[buf][1], qf, qs, ksb + k0 / kQBlock, c, log2_448, kKeyTile, li, g, st, o);
+  }
+  // The last tile when S is not a multiple of the tile: keys >= S masked.
+  if (nfull < ntiles) {
+    const int k0 = nfull * kKeyTile;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-
-    v16i sacc[4];
-    qk_tile(lds_k, qf, li, g, sacc);
-
-    float f[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) f[u] = (qs * ksb[k0 / kQBlock + u]) * c;
-
-    const int nvalid = S - k0;
-    const bool tail = nvalid < kKeyTile;
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (tail && 32 * u >= nvalid) continue;
-      int mx = INT32_MIN;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int a = sacc[u][r];
-        if (tail && key_of(u, r, g) >= nvalid) a = INT32_MIN;
-        mx = max(mx, a);
-      }
-      tmax = fmaxf(tmax, (float)mx * f[u]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m, tmax);
-    const float m2_new = m_new - log2_448;
-    const float alpha = __builtin_amdgcn_exp2f(m2 - m2_new);
-    // Scores beyond 2^19 (log2 units) make the fp32 spacing of m coarse
-    // enough for P' to pass 464, where the conversion would give NaN.
-    const bool big = __ballot(m_new > 524288.0f) != 0;
-
-    float lsum = 0.0f;
-    v8i pop[2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
-          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[u][r], f[u], -m2_new));
-          if (tail && key_of(u, r, g) >= nvalid) pe = 0.0f;
-          lsum += pe;
-          p[e] = big ? fminf(pe, 448.0f) : pe;
-        }
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
-        pop[u >> 1][4 * (u & 1) + j] = wd;
-      }
-    }
-    l = l * alpha + lsum;
-    if (__ballot(alpha != 1.0f) != 0) {
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) o[cb] *= alpha;
-    }
-
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int row = 32 * cb + li;
-        const v4i lo = *(const v4i*)(lds_v + swz(row, 4 * w + 2 * g));
-        const v4i hi = *(const v4i*)(lds_v + swz(row, 4 * w + 2 * g + 1));
-        const v8i vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop[w], o[cb], 0, 0, 0, 0, 0, 0);
-      }
-    }
-    m = m_new;
-    m2 = m2_new;
+    attn_tile<true>(lds[nfull & 1][0], lds[nfull & 1][1], qf, qs, ksb + k0 / kQBlock, c, log2_448, S - k0, li, g,
+                    st, o);
   }
 
   // Epilogue: O = acc * v_scale / l, bf16, layout [B, S, H, D].
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const float lt = pair_sum(st.l);
   const float rl = __fdiv_rn(1.0f, lt);
   const int qi = q0 + li;
   if (qi < S) {

@@ -255,11 +255,19 @@ def test_attention_config_full_compare(idx):
         gate(got[b, :, h, :], ref, ex, f"config {idx} head {h}")
 
 
-def _sample_rows(S, rng, nrand=2):
+def _sample_rows(S, rng, nrand=2, nrows=1024):
+    """First, last (tail) and random 32-row blocks, plus random single rows.
+
+    Whole blocks exercise the per-block scales and the ragged tail; the
+    random rows make the cosine against exact attention a stable estimate
+    for the head (about a quarter of the blocks of the outlier recipe hold an
+    x8 row, and those blocks are far less accurate than the rest).
+    """
     nb = (S + 31) // 32
     blocks = sorted(set([0, nb - 1] + list(rng.choice(nb, nrand, replace=False))))
-    rows = np.concatenate([np.arange(32 * t, min(S, 32 * t + 32)) for t in blocks])
-    return rows
+    rows = np.concatenate([np.arange(32 * t, min(S, 32 * t + 32)) for t in blocks]
+                          + [rng.choice(S, nrows, replace=False)])
+    return np.unique(rows)
 
 
 @pytest.mark.parametrize("idx", [3, 4, 5])
