@@ -113,7 +113,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times), to calibrate "
+                         "the FETCH_SIZE / WRITE_SIZE counters against known bytes, then exit")
     args = ap.parse_args()
+    if args.copy_calibration_mib:
+        import torch
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path runs on a single MI355X and "
               "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)

@@ -122,8 +122,11 @@ sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t
  *   A = q8 . k8^T (exact int32);  c = fl32(fl32(softmax_scale)*fl32(log2 e));
  *   f = fl32(fl32(q_scale*k_scale)*c) per (query block, key block);
  *   t = fl32(A*f); m = running max of t (keys >= S masked);
- *   m2 = fl32(m - fl32(log2 448)); P' = 2^fl32(A*f - m2) (fused multiply-add,
- *   hardware exp2), so P' = 448 * 2^(t - m) up to rounding;
+ *   m2 = fl32(m - fl32(log2 448)); with X = 1.5*2^23 + A (the int32
+ *   accumulator starts from the bit pattern of 1.5*2^23, so it reads as this
+ *   exact float) and C = fl32(fl32(1.5*2^23*f) + m2):
+ *   P' = 2^fl32(X*f - C) (fused multiply-add, hardware exp2), which is
+ *   448 * 2^(t - m) up to rounding;
  *   l = sum of fp32 P' (rescaled by 2^(m2_old - m2) when the max moves);
  *   p8 = E4M3FN(min(P', 448)); acc[c] = sum p8 * v8[c] (FP8 MFMA, fp32
  *   accumulation, same rescaling); out = bf16_rne(acc * v_scale[c] / l).

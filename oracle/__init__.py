@@ -46,6 +46,7 @@ from .attention import (  # noqa: F401
     attention_head,
     exact_attention_fp64,
     exp2_scale,
+    online_softmax_exact,
     online_softmax_pv,
     qk_scores,
     sage_attention,

@@ -21,10 +21,16 @@ Readings taken where the pages are silent, in step order:
    is passed in). Per query row and tile tau:
    m_tau = max(m_{tau-1}, max_{j in tau} t_j)  (m_0 = -inf).
 4. P with the fixed 448 scale, folded into the exponent: m2_tau =
-   fl32(m_tau - fl32(log2 448)); arg_j = fl32(A_j * f - m2_tau) (the exact
-   real value rounded once, i.e. a fused multiply-add); P'_j = fl32(2^arg_j),
-   so P'_j = 448 * 2^(t_j - m_tau) up to rounding and lies in (0, 448].
-   p8_j = E4M3FN(P'_j). The row sum l accumulates the fp32 P'_j.
+   fl32(m_tau - fl32(log2 448)). The score enters the exponent as the fp32
+   value X_j = 1.5 * 2^23 + A_j (exact, since |A| < 2^21: the integer
+   accumulation starts from the bit pattern of 1.5 * 2^23, so it can be read
+   as a float directly); with F = fl32(1.5 * 2^23 * f) and C_tau =
+   fl32(F + m2_tau), arg_j = fl32(X_j * f - C_tau) (the exact real value
+   rounded once, i.e. a fused multiply-add). Mathematically arg_j = A_j f -
+   m2_tau; the two fp32 roundings in C_tau move it by at most about one unit
+   of A_j * f. P'_j = fl32(2^arg_j), so P'_j = 448 * 2^(t_j - m_tau) up to
+   rounding. p8_j = E4M3FN(P'_j) (saturating at 448). The row sum l
+   accumulates the fp32 P'_j.
 5. Across tiles, partial sums are combined with the factors 2^(m2_tau -
    m2_T) of the final tile T (here in float64; the kernel rescales its fp32
    accumulators as it goes, which agrees to fp32 rounding).
@@ -32,10 +38,12 @@ Readings taken where the pages are silent, in step order:
    are exact. Epilogue: O[c] = bf16(acc[c] * v_scale[c] / l), formed in
    float64 and rounded once.
 
-Where the exact value of step 4's subtraction is not representable in float64
-(an exponent gap above ~8 binades between the two terms) the float64 result
-is rounded a second time to fp32; the two roundings disagree with the single
-rounding only when the first lands exactly on an fp32 midpoint.
+Step 4's fused multiply-add is evaluated in float64: X * f is exact there
+(48 significant bits), and so is the subtraction of C_tau whenever the two
+terms are within a factor two of each other (the usual case, as both are near
+1.5 * 2^23 * f); otherwise the float64 result is rounded a second time to
+fp32, which disagrees with a single rounding only when the first lands
+exactly on an fp32 midpoint.
 """
 from __future__ import annotations
 
@@ -48,6 +56,7 @@ from .quant import QK_BLOCK, quant_qk, quant_v
 
 LOG2E = np.float32(math.log2(math.e))
 LOG2_448 = np.float32(math.log2(448.0))
+SCORE_BIAS = 12582912.0          # 1.5 * 2^23
 
 
 def exp2_scale(softmax_scale: float) -> np.float32:
@@ -65,68 +74,77 @@ def qk_scores(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
     return a.astype(np.int64)
 
 
-def online_softmax_pv(x: np.ndarray, vals: np.ndarray, bn: int, quantized: bool = True,
-                      n_valid: int | None = None):
-    """Tile-scheduled online softmax followed by PV, for a set of query rows.
-
-    x:    float64 [R, S] exact scores in the log2 domain (A * f, step 2
-          without the final rounding; for the unquantized path any real
-          scores times log2 e).
-    vals: float64 [S, D] values multiplying P (decoded FP8 V codes when
-          ``quantized``, plain V otherwise).
-    bn:   key tile width.
-    quantized: True follows steps 3-5 with fp32 roundings and FP8 P;
-          False is the same tile loop in float64 with P = 2^(x - m), no
-          rounding and no encoding (used to pin the loop against textbook
-          softmax attention).
-    n_valid: keys at index >= n_valid are masked (count as -inf).
-
-    Returns (acc float64 [R, D], l float64 [R]); the output is acc / l
-    (times v_scale for the quantized path).
-    """
-    x = np.asarray(x, dtype=np.float64)
-    R, S = x.shape
-    if n_valid is None:
-        n_valid = S
-    ntiles = (S + bn - 1) // bn
-    m_prev = np.full(R, -np.inf)
-    shifts = []      # per tile: exponent offset used for that tile's P
-    l_parts = []
-    acc_parts = []
-    for tau in range(ntiles):
-        j0, j1 = tau * bn, min(S, (tau + 1) * bn)
-        j1v = min(j1, n_valid)
-        if j1v <= j0:
-            break
-        xt = x[:, j0:j1v]
-        if quantized:
-            t = f32(xt)                                      # fl32(A * f)
-            m = np.maximum(m_prev, t.max(axis=1).astype(np.float64))
-            m2 = (m.astype(np.float32) - LOG2_448).astype(np.float32)
-            arg = f32(xt - m2.astype(np.float64)[:, None])   # fma, one rounding
-            p = f32(np.exp2(arg.astype(np.float64)))         # P' in fp32
-            p_used = fp8_e4m3fn_decode(fp8_e4m3fn_encode(p))  # dec(E4M3FN(P'))
-            shift = m2.astype(np.float64)
-            l_t = p.astype(np.float64).sum(axis=1)
-        else:
-            m = np.maximum(m_prev, xt.max(axis=1))
-            p = np.exp2(xt - m[:, None])
-            p_used = p
-            shift = m
-            l_t = p.sum(axis=1)
-        acc_t = p_used @ np.asarray(vals[j0:j1v], dtype=np.float64)
-        shifts.append(shift)
-        l_parts.append(l_t)
-        acc_parts.append(acc_t)
-        m_prev = m
+def _combine(shifts, l_parts, acc_parts, D):
+    """Sum per-tile partials with factors 2^(shift_tau - shift_T) (float64)."""
     final = shifts[-1]
-    l = np.zeros(R)
-    acc = np.zeros((R, vals.shape[1]))
+    l = np.zeros(len(final))
+    acc = np.zeros((len(final), D))
     for shift, l_t, acc_t in zip(shifts, l_parts, acc_parts):
         w = np.exp2(shift - final)
         l += w * l_t
         acc += w[:, None] * acc_t
     return acc, l
+
+
+def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None):
+    """Steps 2-5 for a set of query rows: the method's tile-scheduled online
+    softmax with FP8 P, followed by PV.
+
+    A:    int64 [R, S] exact integer scores.
+    f:    float32 [R, S] dequantization factor of each (row, key) pair.
+    vals: float64 [S, D] decoded FP8 V values (natural key order).
+    bn:   key tile width; keys at index >= n_valid are masked.
+    Returns (acc float64 [R, D], l float64 [R]); the output is
+    acc * v_scale / l.
+    """
+    A = np.asarray(A, dtype=np.int64)
+    f = np.asarray(f, dtype=np.float32)
+    R, S = A.shape
+    if n_valid is None:
+        n_valid = S
+    f64 = f.astype(np.float64)
+    x = A.astype(np.float64) * f64                       # A * f, exact
+    X = (A + int(SCORE_BIAS)).astype(np.float64)         # 1.5 * 2^23 + A, exact
+    F = (np.float32(SCORE_BIAS) * f).astype(np.float32)  # fl32(1.5 * 2^23 * f)
+    m_prev = np.full(R, -np.inf)
+    shifts, l_parts, acc_parts = [], [], []
+    for j0 in range(0, min(S, n_valid), bn):
+        j1 = min(S, n_valid, j0 + bn)
+        t = f32(x[:, j0:j1])                             # fl32(A * f)
+        m = np.maximum(m_prev, t.max(axis=1).astype(np.float64))
+        m2 = (m.astype(np.float32) - LOG2_448).astype(np.float32)
+        C = (F[:, j0:j1] + m2[:, None]).astype(np.float32)          # fl32(F + m2)
+        arg = f32(X[:, j0:j1] * f64[:, j0:j1] - C.astype(np.float64))  # fma
+        p = f32(np.exp2(arg.astype(np.float64)))         # P' in fp32
+        p_used = fp8_e4m3fn_decode(fp8_e4m3fn_encode(p))  # dec(E4M3FN(P'))
+        shifts.append(m2.astype(np.float64))
+        l_parts.append(p.astype(np.float64).sum(axis=1))
+        acc_parts.append(p_used @ np.asarray(vals[j0:j1], dtype=np.float64))
+        m_prev = m
+    return _combine(shifts, l_parts, acc_parts, vals.shape[1])
+
+
+def online_softmax_exact(x, vals, bn: int, n_valid: int | None = None):
+    """The same tile loop with quantization switched off: float64 scores x
+    (already in the log2 domain), P = 2^(x - m) with no rounding or encoding.
+    Used to pin the running-max bookkeeping against textbook softmax.
+    Returns (acc, l) with output acc / l."""
+    x = np.asarray(x, dtype=np.float64)
+    R, S = x.shape
+    if n_valid is None:
+        n_valid = S
+    m_prev = np.full(R, -np.inf)
+    shifts, l_parts, acc_parts = [], [], []
+    for j0 in range(0, min(S, n_valid), bn):
+        j1 = min(S, n_valid, j0 + bn)
+        xt = x[:, j0:j1]
+        m = np.maximum(m_prev, xt.max(axis=1))
+        p = np.exp2(xt - m[:, None])
+        shifts.append(m)
+        l_parts.append(p.sum(axis=1))
+        acc_parts.append(p @ np.asarray(vals[j0:j1], dtype=np.float64))
+        m_prev = m
+    return _combine(shifts, l_parts, acc_parts, vals.shape[1])
 
 
 def attention_head(q8, q_scale, k8, k_scale, v8, v_scale, softmax_scale, bn,
@@ -148,9 +166,8 @@ def attention_head(q8, q_scale, k8, k_scale, v8, v_scale, softmax_scale, bn,
     f_blocks = f32(f32(q_scale[rows // QK_BLOCK][:, None].astype(np.float32)
                        * k_scale[None, :].astype(np.float32)) * c)  # [R, nbk]
     f_keys = f_blocks[:, np.arange(S) // QK_BLOCK]               # [R, S] fp32
-    x = A.astype(np.float64) * f_keys.astype(np.float64)        # exact
     vals = fp8_e4m3fn_decode(v8)
-    acc, l = online_softmax_pv(x, vals, bn, quantized=True, n_valid=n_valid)
+    acc, l = online_softmax_pv(A, f_keys, vals, bn, n_valid=n_valid)
     o64 = acc * np.asarray(v_scale, dtype=np.float64)[None, :] / l[:, None]
     o = bf16_round_f64(o64)
     return (o, o64) if return_f64 else o

@@ -139,7 +139,7 @@ sage_status attn_impl(const int8_t* q8, const float* qs, const int8_t* k8, const
   if (nwg > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
   const float c = (float)softmax_scale * (float)1.4426950408889634;  // fl32(fl32(scale) * fl32(log2 e))
   const float log2_448 = (float)std::log2(448.0);
-  hipLaunchKernelGGL(sage::attn_fwd_kernel, dim3((unsigned)nwg), dim3(256), 0, st, q8, qs, k8, ks, vt, vs,
+  hipLaunchKernelGGL(sage::attn_fwd_kernel, dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st, q8, qs, k8, ks, vt, vs,
                      (int)S, (int)H, (int)Sp, nqt, (int)nwg, c, log2_448, (uint16_t*)out);
   return launched("sage_attn_fwd");
 }
@@ -262,7 +262,7 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
     return fail(SAGE_ERR_RANGE, "window outside [0, S_pad)");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
   const int64_t rA = r0 / 32 * 32, cA = c0 / 128 * 128;
-  const int64_t gy = (r0 + nr - rA + sage::kQueryTile - 1) / sage::kQueryTile;
+  const int64_t gy = (r0 + nr - rA + sage::kDebugRows - 1) / sage::kDebugRows;
   const int64_t gx = (c0 + nc - cA + sage::kKeyTile - 1) / sage::kKeyTile;
   if (gx > INT32_MAX || gy > 65535) return fail(SAGE_ERR_RANGE, "window too large");
   hipLaunchKernelGGL(sage::debug_qk_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, (hipStream_t)stream,

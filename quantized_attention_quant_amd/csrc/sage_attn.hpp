@@ -7,6 +7,12 @@
 // E4M3FN with the fixed scale 448 (the largest E4M3FN value), folded into the
 // exponent of exp2.
 //
+// The INT8 score accumulators start at 0x4B400000, the bit pattern of the
+// fp32 value 1.5 * 2^23: since |A| < 2^21, the accumulated integer
+// 0x4B400000 + A is the bit pattern of the exact fp32 value 1.5 * 2^23 + A,
+// so the scores are read as floats without a conversion instruction, and
+// integer order of the biased values is still score order.
+//
 // Work decomposition: one workgroup = 4 waves = 128 queries of one (b, h);
 // each wave owns 32 queries and streams all keys in tiles of 128.
 //   QK:  S^T[key][query] = K . Q^T with v_mfma_i32_32x32x32_i8 (A = K rows
@@ -20,14 +26,17 @@
 //        layout stores keys in the order the score accumulator leaves them,
 //        so no shuffles are needed between the two products.
 // LDS tiles are rows of 128 bytes whose 16-byte chunks are XOR-swizzled by
-// the row index, so the 64 lanes' 16-byte reads hit distinct banks.
+// (row / 2) % 8: a 16-byte read is served for 16 lanes at a time from 64
+// four-byte banks, and the 16 rows a lane group reads then cover all 256
+// bytes of the banks exactly once.
 #pragma once
 
 #include "sage_common.hpp"
 
 namespace sage {
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row)) << 4); }
 
 // Cooperative copy of one 128-row x 128-byte tile (rows `row_stride` bytes
 // apart in global memory) into swizzled LDS. 256 threads, 4 x 16 B each.
@@ -51,12 +60,13 @@ __device__ __forceinline__ void load_q_frag(const int8_t* __restrict__ qrow, v4i
 }
 
 // S^T for the 128 keys of the staged tile against the wave's 32 queries:
-// sacc[u] covers keys [32 u, 32 u + 32) of the tile.
+// sacc[u] covers keys [32 u, 32 u + 32) of the tile; every accumulator
+// starts from `init`.
 __device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ lds_k, const v4i qf[4], int li, int g,
-                                        v16i sacc[4]) {
+                                        const v16i& init, v16i sacc[4]) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    v16i acc = {0};
+    v16i acc = init;
     const int row = 32 * u + li;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -81,7 +91,7 @@ __device__ __forceinline__ void stage_tile_async(uint8_t* lds, const uint8_t* __
   for (int i = 0; i < 16 / kWaves; ++i) {
     const int grp = wave + kWaves * i;
     const int row = 8 * grp + rr;
-    const uint8_t* g = src + row * row_stride + ((cp ^ rr) << 4);
+    const uint8_t* g = src + row * row_stride + ((cp ^ swz_key(row)) << 4);
     __builtin_amdgcn_global_load_lds((const void*)g,
                                      (__attribute__((address_space(3))) void*)(lds + grp * 1024), 16, 0, 0);
   }
@@ -112,14 +122,19 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+constexpr int kScoreBias = 0x4B400000;        // bits of 1.5 * 2^23
+constexpr float kScoreBiasF = 12582912.0f;     // 1.5 * 2^23
+
 // P' = 2^(A f - m2) for the 64 scores of a lane, their fp32 sum, and the
 // E4M3FN codes packed in the FP8 MFMA B-operand order (byte 16 (u%2) + r of
-// pop[u/2] holds sub-tile u, register r). kClamp: saturate before the
-// conversion (the hardware conversion gives NaN above 464). kTail: keys at
-// or past `nvalid` get P' = 0.
+// pop[u/2] holds sub-tile u, register r). With X = 1.5 * 2^23 + A (the biased
+// accumulator read as a float) the exponent is fl32(X f - nc[u]) with
+// nc[u] = fl32(fl32(1.5 * 2^23 * f) + m2), one fused multiply-add.
+// kClamp: saturate before the conversion (the hardware conversion gives NaN
+// above 464). kTail: keys at or past `nvalid` get P' = 0.
 template <bool kClamp, bool kTail>
-__device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], float m2, int nvalid, int g,
-                                           v8i pop[2]) {
+__device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], const float nc[4], int nvalid,
+                                           int g, v8i pop[2]) {
   float lsum = 0.0f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -129,12 +144,14 @@ __device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], fl
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * j + e;
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[u][r], f[u], -m2));
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[u][r]), f[u], -nc[u]));
         if (kTail && key_of(u, r, g) >= nvalid) pe = 0.0f;
         lsum += pe;
         p[e] = kClamp ? fminf(pe, 448.0f) : pe;
       }
-      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      // the first conversion's "old" operand only supplies the upper half,
+      // which the second conversion overwrites
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
       wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
       pop[u >> 1][4 * (u & 1) + j] = wd;
     }
@@ -148,15 +165,18 @@ struct RowState {
 
 // One key tile for one wave: QK^T, online softmax, PV.
 template <bool kTail>
-__device__ __forceinline__ void attn_tile(const uint8_t* lk, const uint8_t* lv, const v4i qf[4], float qs,
+__device__ __forceinline__ void attn_tile(const uint8_t* lk, const uint8_t* lv, const v4i qf[4], const v16i& bias,
+                                          float qs,
                                           const float* __restrict__ ks4, float c, float log2_448, int nvalid,
                                           int li, int g, RowState& st, v16f o[4]) {
   v16i s[4];
-  qk_tile(lk, qf, li, g, s);
+  qk_tile(lk, qf, li, g, bias, s);
   float f[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) f[u] = (qs * ks4[u]) * c;
 
+  // t = fl32(A f) is monotone in A for f >= 0, so the tile max is taken on
+  // the (biased) integers of each 32-key block and dequantized once.
   float tmax = -INFINITY;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -166,23 +186,33 @@ __device__ __forceinline__ void attn_tile(const uint8_t* lk, const uint8_t* lv, 
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (key_of(u, r, g) >= nvalid) sm[r] = INT32_MIN;
-      tmax = fmaxf(tmax, (float)max16(sm) * f[u]);
+      const int mx = max16(sm);
+      if (mx != INT32_MIN) tmax = fmaxf(tmax, (float)(mx - kScoreBias) * f[u]);
     } else {
-      tmax = fmaxf(tmax, (float)max16(s[u]) * f[u]);
+      tmax = fmaxf(tmax, (float)(max16(s[u]) - kScoreBias) * f[u]);
     }
   }
   tmax = pair_max(tmax);
   const float m_new = fmaxf(st.m, tmax);
   const float m2_new = m_new - log2_448;
   const float alpha = __builtin_amdgcn_exp2f(st.m2 - m2_new);
+  float nc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) nc[u] = kScoreBiasF * f[u] + m2_new;
   v8i pop[2];
   float lsum;
-  // Scores beyond 2^19 (log2 units) make the fp32 spacing of m coarse
-  // enough for P' to pass 464; that rare case takes the clamped variant.
-  if (__builtin_expect(__ballot(m_new > 524288.0f) != 0, 0))
-    lsum = softmax_p<true, kTail>(s, f, m2_new, nvalid, g, pop);
+  // P' of the largest score is 448 * 2^e, where e collects the fp32
+  // roundings of m, m2, 1.5 * 2^23 * f and nc. While all of those stay below
+  // 2^17 in magnitude each rounding is at most 2^-7 and P' <= 448 * 2^(1/32)
+  // < 464, the limit of the conversion (above it the hardware gives NaN).
+  // Larger values (outlier-scale Q/K blocks) take the saturating variant.
+  float mag = fabsf(m_new);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) mag = fmaxf(mag, fabsf(nc[u]));
+  if (__builtin_expect(__ballot(mag >= 131072.0f) != 0, 0))
+    lsum = softmax_p<true, kTail>(s, f, nc, nvalid, g, pop);
   else
-    lsum = softmax_p<false, kTail>(s, f, m2_new, nvalid, g, pop);
+    lsum = softmax_p<false, kTail>(s, f, nc, nvalid, g, pop);
   st.l = st.l * alpha + lsum;
   if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
@@ -204,9 +234,7 @@ __device__ __forceinline__ void attn_tile(const uint8_t* lk, const uint8_t* lv, 
   }
 }
 
-constexpr int kAttnWaves = kQueryTile / 32;
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qscale,
                      const int8_t* __restrict__ k8, const float* __restrict__ kscale,
                      const uint8_t* __restrict__ v8t, const float* __restrict__ vscale, int S, int H,
@@ -236,6 +264,9 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   load_q_frag(q8 + ((bh * S_pad + q0 + li) * kHeadDim + 64 * g), qf);
   const float qs = qscale[bh * nbp + q0 / kQBlock];
 
+  v16i bias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bias[r] = kScoreBias;
   RowState st{-INFINITY, -INFINITY, 0.0f};
   v16f o[4];
 #pragma unroll
@@ -252,14 +283,14 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
       stage_tile_async<kAttnWaves>(lds[buf ^ 1][0], kbase + (int64_t)(k0 + kKeyTile) * kHeadDim, kHeadDim, wave, lane);
       stage_tile_async<kAttnWaves>(lds[buf ^ 1][1], vbase + k0 + kKeyTile, S_pad, wave, lane);
     }
-    attn_tile<false>(lds[buf][0], lds[buf][1], qf, qs, ksb + k0 / kQBlock, c, log2_448, kKeyTile, li, g, st, o);
+    attn_tile<false>(lds[buf][0], lds[buf][1], qf, bias, qs, ksb + k0 / kQBlock, c, log2_448, kKeyTile, li, g, st, o);
   }
   // The last tile when S is not a multiple of the tile: keys >= S masked.
   if (nfull < ntiles) {
     const int k0 = nfull * kKeyTile;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    attn_tile<true>(lds[nfull & 1][0], lds[nfull & 1][1], qf, qs, ksb + k0 / kQBlock, c, log2_448, S - k0, li, g,
+    attn_tile<true>(lds[nfull & 1][0], lds[nfull & 1][1], qf, bias, qs, ksb + k0 / kQBlock, c, log2_448, S - k0, li, g,
                     st, o);
   }
 
@@ -287,7 +318,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
 }
 
 // Debug dump of int32 scores through the same staging and MFMA path.
-// grid (key tiles, query tiles of 128), 256 threads.
+// grid (key tiles, query tiles of kDebugRows = 128), 256 threads.
 __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ q8,
                                                        const int8_t* __restrict__ k8, int S_pad,
                                                        int64_t bh, int rA, int r0, int nr, int cA,
@@ -296,14 +327,15 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int k0 = cA + blockIdx.x * kKeyTile;
-  const int qa = rA + blockIdx.y * kQueryTile + wave * 32;
+  const int qa = rA + blockIdx.y * kDebugRows + wave * 32;
   stage_tile(lds_k, (const uint8_t*)k8 + (bh * S_pad + k0) * kHeadDim, kHeadDim, tid);
   __syncthreads();
   if (qa >= S_pad) return;
   v4i qf[4];
   load_q_frag(q8 + ((bh * S_pad + qa + li) * kHeadDim + 64 * g), qf);
   v16i sacc[4];
-  qk_tile(lds_k, qf, li, g, sacc);
+  const v16i zero = {0};
+  qk_tile(lds_k, qf, li, g, zero, sacc);
   const int row = qa + li;
   if (row < r0 || row >= r0 + nr) return;
 #pragma unroll

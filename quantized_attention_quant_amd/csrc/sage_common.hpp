@@ -10,7 +10,12 @@ constexpr int kHeadDim = 128;     // the only head size of the method
 constexpr int kQBlock = 32;       // Q/K quantization block (rows)
 constexpr int kSeqAlign = 256;    // padding of the quantized layouts
 constexpr int kKeyTile = 128;     // BN: keys per online-softmax tile
-constexpr int kQueryTile = 128;   // BM: queries per workgroup (4 waves x 32)
+#ifndef SAGE_ATTN_WAVES
+#define SAGE_ATTN_WAVES 8
+#endif
+constexpr int kAttnWaves = SAGE_ATTN_WAVES;     // waves per attention workgroup
+constexpr int kQueryTile = 32 * kAttnWaves;     // BM: queries per workgroup
+constexpr int kDebugRows = 128;                 // query rows per debug-dump workgroup
 constexpr int kVGroup = 64;       // keys per permuted group of the V^T layout
 constexpr int kVChunkRows = 512;  // rows per partial-amax chunk of V
 

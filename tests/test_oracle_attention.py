@@ -28,7 +28,7 @@ from oracle import (
     attention_head,
     exact_attention_fp64,
     fp8_e4m3fn_decode,
-    online_softmax_pv,
+    online_softmax_exact,
     qk_scores,
     quant_qk,
     quant_v,
@@ -71,7 +71,7 @@ def test_unquantized_tile_loop_is_textbook_softmax(S, bn, n_valid):
     v = rng.standard_normal((1, S, 1, 128))
     nv = S if n_valid is None else n_valid
     x = (q[0, :, 0] @ k[0, :, 0].T) * SCALE * math.log2(math.e)
-    acc, l = online_softmax_pv(x, v[0, :, 0], bn, quantized=False, n_valid=n_valid)
+    acc, l = online_softmax_exact(x, v[0, :, 0], bn, n_valid=n_valid)
     ref = exact_attention_fp64(q[:, :, :, :], k[:, :nv], v[:, :nv], SCALE)
     # exact_attention_fp64 needs equal Q/K lengths only for its loops; emulate
     s = (q[0, :, 0] @ k[0, :nv, 0].T) * SCALE
@@ -83,7 +83,7 @@ def test_unquantized_tile_loop_is_textbook_softmax(S, bn, n_valid):
 def test_unquantized_row_sum_is_one():
     rng = np.random.default_rng(4)
     x = rng.standard_normal((64, 300)) * 20
-    acc, l = online_softmax_pv(x, np.ones((300, 4)), 64, quantized=False)
+    acc, l = online_softmax_exact(x, np.ones((300, 4)), 64)
     assert np.max(np.abs(acc / l[:, None] - 1.0)) < 1e-12
 
 
@@ -284,7 +284,10 @@ def _scalar_method(q, k, v, scale, bn):
                 l *= w
                 acc = [a * w for a in acc]
             for j in js:
-                p = _f32(2.0 ** _f32(A[j] * f[j] - m2))
+                # exponent: fl32(X f - fl32(fl32(1.5 2^23 f) + m2)), X = 1.5 2^23 + A
+                X = 12582912.0 + A[j]
+                C = _f32(_f32(12582912.0 * f[j]) + m2)
+                p = _f32(2.0 ** _f32(X * f[j] - C))
                 l += p
                 p8 = _e4m3_scalar(p)
                 for c in range(D):
