@@ -26,7 +26,8 @@
  *   - No global mutable state besides that string: calls are thread-safe;
  *     calls that share output or workspace buffers must be ordered by the
  *     caller.
- *   - Sizes: B, S, H >= 1, D == 128, B*H*S_pad*128 < 2^62.
+ *   - Sizes: B, S, H >= 1, D == 128, S <= 2^24, B, H <= 2^20 and
+ *     B*H*S_pad*128 < 2^62; larger sizes return SAGE_ERR_SHAPE.
  *   - Inputs containing NaN/Inf, or whose scaled scores overflow fp32, are
  *     outside the contract (no guarantee on the output).
  */

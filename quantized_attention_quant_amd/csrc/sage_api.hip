@@ -41,9 +41,11 @@ sage_status check_shape(int64_t B, int64_t S, int64_t H, int64_t D) {
   if (D != sage::kHeadDim) return fail(SAGE_ERR_UNSUPPORTED, "head dim %lld unsupported (only 128)", (long long)D);
   if (B < 1 || S < 1 || H < 1) return fail(SAGE_ERR_SHAPE, "B, S, H must be >= 1 (got %lld, %lld, %lld)",
                                            (long long)B, (long long)S, (long long)H);
-  // S_pad * B * H * D must stay well inside int64, and S inside int32
-  if (S > (int64_t)1 << 30 || B > (int64_t)1 << 20 || H > (int64_t)1 << 20)
-    return fail(SAGE_ERR_SHAPE, "sizes too large");
+  // S_pad * B * H * D must stay well inside int64, and one head's quantized
+  // K or V^T (S_pad * 128 bytes) inside the 2^31-byte reach of a buffer
+  // descriptor offset
+  if (S > (int64_t)1 << 24 || B > (int64_t)1 << 20 || H > (int64_t)1 << 20)
+    return fail(SAGE_ERR_SHAPE, "sizes too large (S <= 2^24, B, H <= 2^20)");
   const double n = (double)B * (double)H * (double)seq_pad(S) * 128.0;
   if (n >= 4.0e18) return fail(SAGE_ERR_SHAPE, "sizes overflow");
   return SAGE_OK;

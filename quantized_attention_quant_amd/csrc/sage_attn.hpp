@@ -13,7 +13,7 @@
 // so the scores are read as floats without a conversion instruction, and
 // integer order of the biased values is still score order.
 //
-// Work decomposition: one workgroup = 4 waves = 128 queries of one (b, h);
+// Work decomposition: one workgroup = 8 waves = 256 queries of one (b, h);
 // each wave owns 32 queries and streams all keys in tiles of 128.
 //   QK:  S^T[key][query] = K . Q^T with v_mfma_i32_32x32x32_i8 (A = K rows
 //        from LDS, B = the wave's Q rows kept in VGPRs). Lane l then holds
@@ -79,24 +79,6 @@ __device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ lds_k, const
 
 __device__ __forceinline__ int key_of(int u, int r, int g) { return 32 * u + 8 * (r >> 2) + 4 * g + (r & 3); }
 
-// Asynchronous copy of one 128-row x 128-byte tile into swizzled LDS with
-// global_load_lds_dwordx4: each wave instruction writes 1 KB (8 rows)
-// contiguously, lane l at +16 l, so the swizzle is applied by choosing each
-// lane's source chunk. kWaves waves split the 16 row groups.
-template <int kWaves>
-__device__ __forceinline__ void stage_tile_async(uint8_t* lds, const uint8_t* __restrict__ src, int64_t row_stride,
-                                                 int wave, int lane) {
-  const int rr = lane >> 3, cp = lane & 7;
-#pragma unroll
-  for (int i = 0; i < 16 / kWaves; ++i) {
-    const int grp = wave + kWaves * i;
-    const int row = 8 * grp + rr;
-    const uint8_t* g = src + row * row_stride + ((cp ^ swz_key(row)) << 4);
-    __builtin_amdgcn_global_load_lds((const void*)g,
-                                     (__attribute__((address_space(3))) void*)(lds + grp * 1024), 16, 0, 0);
-  }
-}
-
 __device__ __forceinline__ int imax3(int a, int b, int c) { return max(max(a, b), c); }
 
 // Largest of the 16 scores a lane holds for one sub-tile.
@@ -135,7 +117,8 @@ constexpr float kScoreBiasF = 12582912.0f;     // 1.5 * 2^23
 template <bool kClamp, bool kTail>
 __device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], const float nc[4], int nvalid,
                                            int g, v8i pop[2]) {
-  float lsum = 0.0f;
+  // eight independent partial sums keep the additions off the critical path
+  float ls[8];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -146,7 +129,8 @@ __device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], co
         const int r = 4 * j + e;
         float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[u][r]), f[u], -nc[u]));
         if (kTail && key_of(u, r, g) >= nvalid) pe = 0.0f;
-        lsum += pe;
+        const int k = 4 * (j & 1) + e;
+        ls[k] = (u == 0 && j < 2) ? pe : ls[k] + pe;
         p[e] = kClamp ? fminf(pe, 448.0f) : pe;
       }
       // the first conversion's "old" operand only supplies the upper half,
@@ -156,21 +140,52 @@ __device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], co
       pop[u >> 1][4 * (u & 1) + j] = wd;
     }
   }
-  return lsum;
+  return ((ls[0] + ls[1]) + (ls[2] + ls[3])) + ((ls[4] + ls[5]) + (ls[6] + ls[7]));
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from a buffer into LDS: lane l writes LDS bytes
+// [m0 + 16 l, m0 + 16 l + 16). Written as assembly so that the compiler does
+// not treat the copy as a store that every later LDS read may alias (it
+// would wait for the copy to land before the first read); completion is
+// awaited explicitly with vmcnt before the barrier that publishes the tile.
+// (M0 is reserved by the compiler, which never keeps a value in it across
+// this code; the clobber only documents the write.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const v4i& rsrc, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until every tile copy this wave issued has landed in LDS. The
+// assembly form emits the wait; the builtin tells the compiler's own counter
+// tracking that all vector-memory loads before this point are complete.
+__device__ __forceinline__ void wait_tiles() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unchanged
 }
 
 struct RowState {
   float m, m2, l;
 };
 
-// One key tile for one wave: QK^T, online softmax, PV.
+// Vector phase of one key tile for one wave: running max, rescale of l and
+// O, P' and its FP8 codes.
 template <bool kTail>
-__device__ __forceinline__ void attn_tile(const uint8_t* lk, const uint8_t* lv, const v4i qf[4], const v16i& bias,
-                                          float qs,
-                                          const float* __restrict__ ks4, float c, float log2_448, int nvalid,
-                                          int li, int g, RowState& st, v16f o[4]) {
-  v16i s[4];
-  qk_tile(lk, qf, li, g, bias, s);
+__device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const float* __restrict__ ks4, float c,
+                                             float log2_448, int nvalid, int g, RowState& st, v16f o[4],
+                                             v8i pop[2]) {
   float f[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) f[u] = (qs * ks4[u]) * c;
@@ -199,7 +214,6 @@ __device__ __forceinline__ void attn_tile(const uint8_t* lk, const uint8_t* lv, 
   float nc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) nc[u] = kScoreBiasF * f[u] + m2_new;
-  v8i pop[2];
   float lsum;
   // P' of the largest score is 448 * 2^e, where e collects the fp32
   // roundings of m, m2, 1.5 * 2^23 * f and nc. While all of those stay below
@@ -220,7 +234,10 @@ __device__ __forceinline__ void attn_tile(const uint8_t* lk, const uint8_t* lv, 
   }
   st.m = m_new;
   st.m2 = m2_new;
+}
 
+// O^T += V^T . P^T for one 128-key tile (8 FP8 MFMAs).
+__device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int li, int g, v16f o[4]) {
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
 #pragma unroll
@@ -234,31 +251,82 @@ __device__ __forceinline__ void attn_tile(const uint8_t* lk, const uint8_t* lv, 
   }
 }
 
+// One workgroup = 8 waves = 256 queries of one (b, h); each wave owns 32
+// queries and streams every key tile. Waves w and w + 4 run on the same SIMD.
+// Per tile a wave has a matrix phase (QK^T of the tile, PV of the previous
+// one) and a vector phase (online softmax). Between two barriers, waves 0-3
+// run vector then matrix phase and waves 4-7 matrix then vector phase, so
+// that on each SIMD one wave's exp/FMA work meets the other wave's MFMAs:
+//   interval i, waves 0-3: softmax(i), PV(i), QK(i+1)
+//   interval i, waves 4-7: PV(i-1), QK(i), softmax(i)
+// (waves 0-3 compute QK(0) before interval 0; waves 4-7 compute PV(T-1)
+// after the last one). Interval i reads K tiles i, i+1 and V tiles i-1, i,
+// and loads K tile i+2 and V tile i+1 into the third slot of each
+// three-stage LDS ring.
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qscale,
                      const int8_t* __restrict__ k8, const float* __restrict__ kscale,
                      const uint8_t* __restrict__ v8t, const float* __restrict__ vscale, int S, int H,
                      int S_pad, int nqt, int num_wg, float c, float log2_448,
                      uint16_t* __restrict__ out) {
-  // two stages of (K tile, V^T tile), 16 KB each
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kKeyTile * 128];
+  static_assert(kAttnWaves == 8, "the phase skew pairs waves w and w + 4");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[3][kKeyTile * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[3][kKeyTile * 128];
 
   const int wg = xcd_remap(blockIdx.x, num_wg);
   const int qt = wg % nqt;
   const int64_t bh = wg / nqt;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const bool lead = wave_s < 4;
   const int q0 = qt * kQueryTile + wave * 32;
   const int nbp = S_pad / kQBlock;
 
   const uint8_t* kbase = (const uint8_t*)k8 + bh * S_pad * kHeadDim;
   const uint8_t* vbase = v8t + bh * kHeadDim * (int64_t)S_pad;
   const float* ksb = kscale + bh * nbp;
-  const int ntiles = (S + kKeyTile - 1) / kKeyTile;
-  const int nfull = S / kKeyTile;   // tiles with no masked key
+  const int T = (S + kKeyTile - 1) / kKeyTile;
+  const bool ragged = (S % kKeyTile) != 0;
 
-  stage_tile_async<kAttnWaves>(lds[0][0], kbase, kHeadDim, wave, lane);
-  stage_tile_async<kAttnWaves>(lds[0][1], vbase, S_pad, wave, lane);
+  // Tiles stream into LDS with buffer_load ... lds: lane l of a wave
+  // instruction writes LDS bytes [16 l, 16 l + 16) of an 8-row group, i.e.
+  // row 8 grp + l/8 and swizzled chunk l%8, so it reads source chunk
+  // (l%8) ^ key(row). The lane offsets are loop-invariant; the tile offset is
+  // a scalar. Buffer descriptors cover this head's K rows and V^T rows
+  // (base, stride 0, size in bytes < 2^31, default data format).
+  const uint64_t kaddr = (uint64_t)(uintptr_t)kbase, vaddr = (uint64_t)(uintptr_t)vbase;
+  const uint32_t nbytes = (uint32_t)S_pad * kHeadDim;
+  const v4i rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)kaddr),
+                  __builtin_amdgcn_readfirstlane((int)(uint32_t)(kaddr >> 32) & 0xFFFF),
+                  __builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000};
+  const v4i rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)vaddr),
+                  __builtin_amdgcn_readfirstlane((int)(uint32_t)(vaddr >> 32) & 0xFFFF),
+                  __builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000};
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * (wave + 8 * i) + (lane >> 3);
+    const int chunk = ((lane & 7) ^ swz_key(row)) << 4;
+    koff[i] = (uint32_t)(row * kHeadDim + chunk);
+    voff[i] = (uint32_t)(row * S_pad + chunk);
+  }
+  // LDS byte address of the first 1 KB row group this wave writes per slot.
+  const uint32_t kl0 = lds_addr(lds_k[0]) + wave_s * 1024, vl0 = lds_addr(lds_v[0]) + wave_s * 1024;
+  auto load_k = [&](int t, int slot) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma16(rk, kl0 + slot * (kKeyTile * 128) + i * 8192, koff[i], (uint32_t)t * (kKeyTile * kHeadDim));
+  };
+  auto load_v = [&](int t, int slot) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      dma16(rv, vl0 + slot * (kKeyTile * 128) + i * 8192, voff[i], (uint32_t)t * kKeyTile);
+  };
+
+  load_k(0, 0);
+  load_v(0, 0);
+  if (T > 1) load_k(1, 1);
 
   v4i qf[4];
   load_q_frag(q8 + ((bh * S_pad + q0 + li) * kHeadDim + 64 * g), qf);
@@ -271,27 +339,48 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   v16f o[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) o[cb] = (v16f){0};
+  v16i s[4];
+  v8i pop[2];
 
-  // Full tiles: tile kt+1 streams into the other LDS stage while tile kt is
-  // computed; one barrier per tile.
-  for (int kt = 0; kt < nfull; ++kt) {
-    const int k0 = kt * kKeyTile;
-    const int buf = kt & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < ntiles) {
-      stage_tile_async<kAttnWaves>(lds[buf ^ 1][0], kbase + (int64_t)(k0 + kKeyTile) * kHeadDim, kHeadDim, wave, lane);
-      stage_tile_async<kAttnWaves>(lds[buf ^ 1][1], vbase + k0 + kKeyTile, S_pad, wave, lane);
+  wait_tiles();
+  __syncthreads();
+
+  // The two wave groups run separate loops with the same barrier count:
+  // interval i (0 <= i < T-1) ends with a barrier; tile i lives in slot
+  // i % 3 of both rings. The last interval (i = T-1), whose tile may be
+  // ragged (keys >= S masked), has no barrier after it.
+  if (lead) {
+    qk_tile(lds_k[0], qf, li, g, bias, s);
+    for (int i = 0; i < T - 1; ++i) {
+      const int sl = i % 3;
+      if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
+      load_v(i + 1, (sl + 1) % 3);
+      vector_phase<false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
+      pv_tile(lds_v[sl], pop, li, g, o);
+      qk_tile(lds_k[(sl + 1) % 3], qf, li, g, bias, s);
+      wait_tiles();
+      __syncthreads();
     }
-    attn_tile<false>(lds[buf][0], lds[buf][1], qf, bias, qs, ksb + k0 / kQBlock, c, log2_448, kKeyTile, li, g, st, o);
-  }
-  // The last tile when S is not a multiple of the tile: keys >= S masked.
-  if (nfull < ntiles) {
-    const int k0 = nfull * kKeyTile;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    attn_tile<true>(lds[nfull & 1][0], lds[nfull & 1][1], qf, bias, qs, ksb + k0 / kQBlock, c, log2_448, S - k0, li, g,
-                    st, o);
+    const int i = T - 1;
+    vector_phase<true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, S - i * kKeyTile, g, st, o, pop);
+    pv_tile(lds_v[i % 3], pop, li, g, o);
+  } else {
+    for (int i = 0; i < T - 1; ++i) {
+      const int sl = i % 3;
+      if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
+      load_v(i + 1, (sl + 1) % 3);
+      if (i > 0) pv_tile(lds_v[(sl + 2) % 3], pop, li, g, o);
+      qk_tile(lds_k[sl], qf, li, g, bias, s);
+      vector_phase<false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
+      wait_tiles();
+      __syncthreads();
+    }
+    const int i = T - 1;
+    const int sl = i % 3;
+    if (i > 0) pv_tile(lds_v[(sl + 2) % 3], pop, li, g, o);
+    qk_tile(lds_k[sl], qf, li, g, bias, s);
+    vector_phase<true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, S - i * kKeyTile, g, st, o, pop);
+    pv_tile(lds_v[sl], pop, li, g, o);
   }
 
   // Epilogue: O = acc * v_scale / l, bf16, layout [B, S, H, D].

@@ -75,6 +75,7 @@ def test_validation_codes():
     assert _call("sage_quant_qk", f, 0, 256, 2, 128, f, f, z) == ERR_SHAPE
     assert _call("sage_quant_qk", f, 1, -5, 2, 128, f, f, z) == ERR_SHAPE
     assert _call("sage_quant_qk", f, 1, 1 << 40, 2, 128, f, f, z) == ERR_SHAPE
+    assert _call("sage_quant_qk", f, 1, (1 << 24) + 1, 2, 128, f, f, z) == ERR_SHAPE
     # pointers
     assert _call("sage_quant_qk", z, 1, 256, 2, 128, f, f, z) == ERR_NULL
     assert _call("sage_quant_qk", m, 1, 256, 2, 128, f, f, z) == ERR_ALIGN
