@@ -161,6 +161,75 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
                                  int64_t nr, int64_t c0, int64_t nc, int32_t* scores,
                                  void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Extensions beyond the gfx1201 operation: log-sum-exp output, query and
+ * key/value sequences of different lengths, and optional K smoothing.
+ * ------------------------------------------------------------------------- */
+
+/* Flags of sage_attention_ex. */
+#define SAGE_SMOOTH_K 1u  /* quantize K - mean_s(K) instead of K (sage_quant_k_smooth) */
+
+/* Bytes of scratch sage_quant_k_smooth needs (per-block channel sums). */
+size_t sage_k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
+
+/*
+ * sage_quant_k_smooth - K smoothing followed by sage_quant_qk's INT8
+ * quantization. The pages name K smoothing as SageAttention's default option
+ * and measure it on and off (InvokeAI PR #9657, "feat(attention): add opt-in
+ * SageAttention backend for diffusion models", sections "How it works" and
+ * "QA Instructions"); it subtracts the mean of K over the sequence per
+ * (b, h, channel), to which exact softmax is invariant because every score
+ * of a query row moves by the same amount.
+ *   k        bf16 [B, S, H, D], contiguous.
+ *   k_i8     int8 [B, H, S_pad, D] out; k_scale fp32 [B, H, S_pad/32] out
+ *            (as sage_quant_qk, applied to the smoothed values).
+ *   k_mean   fp32 [B, H, D] out.
+ *   scratch  device memory of sage_k_smooth_scratch_bytes(...) bytes.
+ * Per channel c of (b, h): for each 32-row block t, bsum[t] = fp32 sum of
+ * k[s] over the block's valid rows, added one row at a time in increasing
+ * s; sum = fp32 sum of bsum[t] in increasing t; k_mean = fl32(sum / S). The
+ * values quantized are fl32(k - k_mean) on rows s < S (padded rows stay 0).
+ */
+sage_status sage_quant_k_smooth(const void* k, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* k_i8,
+                                float* k_scale, float* k_mean, void* scratch, size_t scratch_bytes,
+                                void* stream);
+
+/*
+ * sage_attn_fwd_ex - sage_attn_fwd with a query sequence of Sq rows and a
+ * key/value sequence of Skv rows (cross-attention), and an optional
+ * log-sum-exp output. The pages' operation falls back for unequal Q/K/V
+ * shapes and returns no LSE, which keeps ring attention from using it
+ * (diffusers PR #15060, "Add aiter_sage_hub attention backend for AMD RDNA4
+ * (gfx1201)", section "What does this PR do?").
+ *   q_i8, q_scale   from sage_quant_qk on Q [B, Sq, H, D] (S_pad = sage_seq_pad(Sq)).
+ *   k_i8, k_scale   from sage_quant_qk or sage_quant_k_smooth on K [B, Skv, H, D].
+ *   v_fp8_t, v_scale from sage_quant_v on V [B, Skv, H, D].
+ *   out  bf16 [B, Sq, H, D].
+ *   lse  fp32 [B, H, Sq] or NULL (4-byte aligned): per query row,
+ *        ln(sum_j exp(softmax_scale * q.k_j)) of the dequantized scores,
+ *        formed from the kernel's state as ln2 * (m2 + log2 l) (m2 and l as
+ *        in sage_attn_fwd after the last key tile).
+ * sage_attn_fwd(..., S, ...) equals sage_attn_fwd_ex(..., S, S, ..., NULL).
+ */
+sage_status sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                             const uint8_t* v_fp8_t, const float* v_scale, int64_t B, int64_t Sq, int64_t Skv,
+                             int64_t H, int64_t D, float softmax_scale, void* out, float* lse, void* stream);
+
+/* Bytes of workspace sage_attention_ex needs (any flags). 0 on bad sizes. */
+size_t sage_workspace_bytes_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D);
+
+/*
+ * sage_attention_ex - one call for q bf16 [B, Sq, H, D] and k, v bf16
+ * [B, Skv, H, D]: sage_quant_qk(Q), sage_quant_qk(K) (or, with
+ * SAGE_SMOOTH_K, sage_quant_k_smooth(K)), sage_quant_v(V) and
+ * sage_attn_fwd_ex, intermediates in the caller's workspace
+ * (>= sage_workspace_bytes_ex bytes, 256-byte aligned). lse may be NULL.
+ * Unknown flag bits return SAGE_ERR_UNSUPPORTED.
+ */
+sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64_t B, int64_t Sq, int64_t Skv,
+                              int64_t H, int64_t D, float softmax_scale, unsigned flags, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,10 +9,12 @@ It is a plain, slow, numpy implementation of what the method computes, in the
 order the method states it, written for a reader to check by eye:
 
 * ``formats``   - OCP FP8 E4M3FN encoding/decoding and bfloat16 rounding;
-* ``quant``     - symmetric INT8 per 32-row block for Q/K, FP8 per channel for V;
+* ``quant``     - symmetric INT8 per 32-row block for Q/K, FP8 per channel for V,
+  and the optional K smoothing (K minus its mean over the sequence);
 * ``attention`` - exact integer QK^T, dequantization, tile-scheduled online
-  softmax in fp32, P to FP8 with the fixed 448 scale, PV, and the epilogue;
-  plus exact fp64 softmax attention as an independent reference.
+  softmax in fp32, P to FP8 with the fixed 448 scale, PV, the epilogue and
+  the per-row log-sum-exp; query and key lengths may differ; plus exact fp64
+  softmax attention as an independent reference.
 
 Sources (cited by page title and section throughout):
 
@@ -39,13 +41,14 @@ from .formats import (  # noqa: F401
     fp8_e4m3fn_decode,
     fp8_e4m3fn_encode,
 )
-from .quant import quant_qk, quant_v  # noqa: F401
+from .quant import k_mean, quant_k_smooth, quant_qk, quant_v  # noqa: F401
 from .attention import (  # noqa: F401
     LOG2_448,
     LOG2E,
     attention_head,
     exact_attention_fp64,
     exp2_scale,
+    lse_from_state,
     online_softmax_exact,
     online_softmax_pv,
     qk_scores,

@@ -52,7 +52,7 @@ import math
 import numpy as np
 
 from .formats import bf16_round_f64, f32, fp8_e4m3fn_decode, fp8_e4m3fn_encode
-from .quant import QK_BLOCK, quant_qk, quant_v
+from .quant import QK_BLOCK, quant_k_smooth, quant_qk, quant_v
 
 LOG2E = np.float32(math.log2(math.e))
 LOG2_448 = np.float32(math.log2(448.0))
@@ -74,8 +74,10 @@ def qk_scores(q8: np.ndarray, k8: np.ndarray) -> np.ndarray:
     return a.astype(np.int64)
 
 
-def _combine(shifts, l_parts, acc_parts, D):
-    """Sum per-tile partials with factors 2^(shift_tau - shift_T) (float64)."""
+def _combine(shifts, l_parts, acc_parts, D, with_shift=False):
+    """Sum per-tile partials with factors 2^(shift_tau - shift_T) (float64).
+
+    Returns (acc, l), or (acc, l, shift_T) with ``with_shift``."""
     final = shifts[-1]
     l = np.zeros(len(final))
     acc = np.zeros((len(final), D))
@@ -83,10 +85,10 @@ def _combine(shifts, l_parts, acc_parts, D):
         w = np.exp2(shift - final)
         l += w * l_t
         acc += w[:, None] * acc_t
-    return acc, l
+    return (acc, l, final) if with_shift else (acc, l)
 
 
-def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None):
+def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None, with_shift: bool = False):
     """Steps 2-5 for a set of query rows: the method's tile-scheduled online
     softmax with FP8 P, followed by PV.
 
@@ -95,7 +97,8 @@ def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None):
     vals: float64 [S, D] decoded FP8 V values (natural key order).
     bn:   key tile width; keys at index >= n_valid are masked.
     Returns (acc float64 [R, D], l float64 [R]); the output is
-    acc * v_scale / l.
+    acc * v_scale / l. With ``with_shift`` also m2 of the last tile (float64
+    holding fp32 values): l = sum_j 2^(t_j - m2_T) up to rounding.
     """
     A = np.asarray(A, dtype=np.int64)
     f = np.asarray(f, dtype=np.float32)
@@ -121,7 +124,7 @@ def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None):
         l_parts.append(p.astype(np.float64).sum(axis=1))
         acc_parts.append(p_used @ np.asarray(vals[j0:j1], dtype=np.float64))
         m_prev = m
-    return _combine(shifts, l_parts, acc_parts, vals.shape[1])
+    return _combine(shifts, l_parts, acc_parts, vals.shape[1], with_shift)
 
 
 def online_softmax_exact(x, vals, bn: int, n_valid: int | None = None):
@@ -147,63 +150,100 @@ def online_softmax_exact(x, vals, bn: int, n_valid: int | None = None):
     return _combine(shifts, l_parts, acc_parts, vals.shape[1])
 
 
+def lse_from_state(m2_final, l):
+    """Log-sum-exp of a row's scaled scores from the online-softmax state.
+
+    l = sum_j 2^(t_j - m2_T) with t_j = softmax_scale * log2(e) * score_j, so
+    ln sum_j exp(softmax_scale * score_j) = ln 2 * (m2_T + log2 l). Formed in
+    float64 and rounded once to fp32 (the output type). Reading: the pages
+    only say that ring attention needs the LSE (diffusers PR #15060, "What
+    does this PR do?"); natural log, per query row, of the scaled dequantized
+    scores.
+    """
+    m2_final = np.asarray(m2_final, dtype=np.float64)
+    l = np.asarray(l, dtype=np.float64)
+    return f32(math.log(2.0) * (m2_final + np.log2(l)))
+
+
 def attention_head(q8, q_scale, k8, k_scale, v8, v_scale, softmax_scale, bn,
-                   rows=None, n_valid=None, return_f64=False):
+                   rows=None, n_valid=None, return_f64=False, return_lse=False):
     """Quantized attention output for one (batch, head).
 
-    q8, k8: int8 [S, D]; q_scale, k_scale: fp32 [ceil(S/32)];
-    v8: uint8 E4M3FN codes [S, D] (natural key order); v_scale: fp32 [D].
+    q8: int8 [Sq, D], q_scale: fp32 [ceil(Sq/32)]; k8: int8 [Skv, D],
+    k_scale: fp32 [ceil(Skv/32)]; v8: uint8 E4M3FN codes [Skv, D] (natural
+    key order); v_scale: fp32 [D]. Sq and Skv may differ (cross-attention).
     rows: query indices to compute (default: all).
-    Returns bf16-valued float32 [len(rows), D] (and the float64 value before
-    the final rounding if ``return_f64``).
+    Returns bf16-valued float32 [len(rows), D]; with ``return_f64`` also the
+    float64 value before the final rounding; with ``return_lse`` also the
+    fp32 log-sum-exp of each row (``lse_from_state``).
     """
     S = k8.shape[0]
     if rows is None:
         rows = np.arange(q8.shape[0])
     rows = np.asarray(rows)
     c = exp2_scale(softmax_scale)
-    A = qk_scores(q8[rows], k8)                                  # [R, S] exact
+    A = qk_scores(q8[rows], k8)                                  # [R, Skv] exact
     f_blocks = f32(f32(q_scale[rows // QK_BLOCK][:, None].astype(np.float32)
                        * k_scale[None, :].astype(np.float32)) * c)  # [R, nbk]
-    f_keys = f_blocks[:, np.arange(S) // QK_BLOCK]               # [R, S] fp32
+    f_keys = f_blocks[:, np.arange(S) // QK_BLOCK]               # [R, Skv] fp32
     vals = fp8_e4m3fn_decode(v8)
-    acc, l = online_softmax_pv(A, f_keys, vals, bn, n_valid=n_valid)
+    acc, l, m2_final = online_softmax_pv(A, f_keys, vals, bn, n_valid=n_valid, with_shift=True)
     o64 = acc * np.asarray(v_scale, dtype=np.float64)[None, :] / l[:, None]
     o = bf16_round_f64(o64)
-    return (o, o64) if return_f64 else o
+    res = [o]
+    if return_f64:
+        res.append(o64)
+    if return_lse:
+        res.append(lse_from_state(m2_final, l))
+    return tuple(res) if len(res) > 1 else o
 
 
-def sage_attention(q, k, v, softmax_scale, bn, rows=None, heads=None):
-    """Whole method on bf16-valued float32 [B, S, H, D] inputs.
+def sage_attention(q, k, v, softmax_scale, bn, rows=None, heads=None, smooth_k=False, return_lse=False):
+    """Whole method on bf16-valued float32 inputs: q [B, Sq, H, D], k and v
+    [B, Skv, H, D] (Sq = Skv for the pages' operation; they may differ for
+    cross-attention). ``smooth_k`` quantizes K with ``quant_k_smooth``.
 
-    Returns O as float32 [B, S, H, D] holding bf16 values. With ``rows``
-    (query indices) and/or ``heads`` (list of (b, h)), only those are
-    computed and the rest of the output is NaN.
+    Returns O as float32 [B, Sq, H, D] holding bf16 values (and, with
+    ``return_lse``, the fp32 log-sum-exp [B, H, Sq]). With ``rows`` (query
+    indices) and/or ``heads`` (list of (b, h)), only those are computed and
+    the rest is NaN.
     """
-    B, S, H, D = q.shape
+    B, Sq, H, D = q.shape
     q8, qs = quant_qk(q)
-    k8, ks = quant_qk(k)
+    if smooth_k:
+        k8, ks, _ = quant_k_smooth(k)
+    else:
+        k8, ks = quant_qk(k)
     v8, vs = quant_v(v)
-    out = np.full((B, S, H, D), np.nan, dtype=np.float32)
+    out = np.full((B, Sq, H, D), np.nan, dtype=np.float32)
+    lse = np.full((B, H, Sq), np.nan, dtype=np.float32)
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
-    rws = np.arange(S) if rows is None else np.asarray(rows)
+    rws = np.arange(Sq) if rows is None else np.asarray(rows)
     for b, h in pairs:
-        out[b, rws, h, :] = attention_head(q8[b, h], qs[b, h], k8[b, h], ks[b, h],
-                                           v8[b, h], vs[b, h], softmax_scale, bn, rows=rws)
-    return out
+        o, ls = attention_head(q8[b, h], qs[b, h], k8[b, h], ks[b, h], v8[b, h], vs[b, h],
+                               softmax_scale, bn, rows=rws, return_lse=True)
+        out[b, rws, h, :] = o
+        lse[b, h, rws] = ls
+    return (out, lse) if return_lse else out
 
 
-def exact_attention_fp64(q, k, v, softmax_scale):
-    """Textbook softmax(q k^T * scale) v per (b, h), in float64; [B, S, H, D]."""
+def exact_attention_fp64(q, k, v, softmax_scale, return_lse=False):
+    """Textbook softmax(q k^T * scale) v per (b, h), in float64.
+
+    q [B, Sq, H, D], k and v [B, Skv, H, D]; returns [B, Sq, H, D] (and, with
+    ``return_lse``, ln sum_j exp(scale * q.k_j) as float64 [B, H, Sq])."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    B, S, H, D = q.shape
-    out = np.empty((B, S, H, D))
+    B, Sq, H, D = q.shape
+    out = np.empty((B, Sq, H, D))
+    lse = np.empty((B, H, Sq))
     for b in range(B):
         for h in range(H):
             s = (q[b, :, h, :] @ k[b, :, h, :].T) * softmax_scale
-            s = s - s.max(axis=1, keepdims=True)
-            p = np.exp(s)
-            out[b, :, h, :] = (p @ v[b, :, h, :]) / p.sum(axis=1, keepdims=True)
-    return out
+            mx = s.max(axis=1, keepdims=True)
+            p = np.exp(s - mx)
+            den = p.sum(axis=1, keepdims=True)
+            out[b, :, h, :] = (p @ v[b, :, h, :]) / den
+            lse[b, h] = (mx + np.log(den))[:, 0]
+    return (out, lse) if return_lse else out

@@ -18,6 +18,12 @@ Readings taken where the pages are silent:
 * V maps its per-channel amax (over the whole sequence) to 448, the largest
   E4M3FN value: v_scale = amax/448, v8 = E4M3FN(fl32(v * (448/amax)));
 * amax = 0 or a non-finite reciprocal gives scale 0 and all-zero codes.
+
+K smoothing (``k_mean``, ``quant_k_smooth``) is the option InvokeAI PR #9657
+measures on and off (sections "How it works" and "QA Instructions"); the
+pages do not define it. Reading: K - mean_s(K) per (batch, head, channel),
+quantized like K; the fp32 summation order of the mean is fixed in
+``k_mean`` so that the INT8 codes are reproducible bit for bit.
 """
 from __future__ import annotations
 
@@ -88,3 +94,40 @@ def quant_v(v: np.ndarray):
             v8[b, h] = fp8_e4m3fn_encode(y)
             vscale[b, h] = scale
     return v8, vscale
+
+
+def k_mean(k: np.ndarray) -> np.ndarray:
+    """Per-(b, h, channel) mean of K over the sequence, in fp32.
+
+    k: float32 [B, S, H, D] holding bfloat16 values. Reading of the summation
+    order: within each 32-row block the rows are added one at a time in
+    increasing s (fp32, starting from 0); the block sums are then added one
+    at a time in block order; mean = fl32(sum / S).
+    Returns float32 [B, H, D].
+    """
+    k = np.asarray(k, dtype=np.float32)
+    B, S, H, D = k.shape
+    nb = (S + QK_BLOCK - 1) // QK_BLOCK
+    x = np.zeros((B, H, nb * QK_BLOCK, D), dtype=np.float32)
+    x[:, :, :S, :] = k.transpose(0, 2, 1, 3)
+    blocks = x.reshape(B, H, nb, QK_BLOCK, D)
+    bsum = np.zeros((B, H, nb, D), dtype=np.float32)
+    for r in range(QK_BLOCK):                      # rows of a block, in order
+        bsum = (bsum + blocks[:, :, :, r, :]).astype(np.float32)
+    total = np.zeros((B, H, D), dtype=np.float32)
+    for t in range(nb):                            # blocks, in order
+        total = (total + bsum[:, :, t, :]).astype(np.float32)
+    return (total / np.float32(S)).astype(np.float32)
+
+
+def quant_k_smooth(k: np.ndarray):
+    """K smoothing then INT8 quantization: quant_qk(fl32(k - k_mean(k))).
+
+    Returns (k8 int8 [B, H, S, D], scale float32 [B, H, ceil(S/32)],
+             mean float32 [B, H, D]).
+    """
+    k = np.asarray(k, dtype=np.float32)
+    mean = k_mean(k)
+    smoothed = (k - mean[:, None, :, :]).astype(np.float32)   # fl32(k - mean)
+    k8, scales = quant_qk(smoothed)
+    return k8, scales, mean

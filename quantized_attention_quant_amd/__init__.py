@@ -19,7 +19,11 @@ __all__ = [
     "SageError", "lib", "library_path", "sage_abi_version", "sage_kv_tile", "sage_seq_pad",
     "sage_workspace_bytes", "sage_quant_v_scratch_bytes", "sage_quant_qk", "sage_quant_v",
     "sage_attn_fwd", "sage_attention", "sage_debug_qk_scores", "v_key_order",
+    "SAGE_SMOOTH_K", "sage_k_smooth_scratch_bytes", "sage_quant_k_smooth", "sage_attn_fwd_ex",
+    "sage_workspace_bytes_ex", "sage_attention_ex",
 ]
+
+SAGE_SMOOTH_K = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libsage.so")
@@ -59,6 +63,12 @@ def lib() -> ctypes.CDLL:
         "sage_attention": (ctypes.c_int, [p, p, p, i64, i64, i64, i64, f32, p, p, sz, p]),
         "sage_debug_qk_scores": (ctypes.c_int, [p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                                 i64, p, p]),
+        "sage_k_smooth_scratch_bytes": (sz, [i64, i64, i64, i64]),
+        "sage_quant_k_smooth": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p, p, sz, p]),
+        "sage_attn_fwd_ex": (ctypes.c_int, [p, p, p, p, p, p, i64, i64, i64, i64, i64, f32, p, p, p]),
+        "sage_workspace_bytes_ex": (sz, [i64, i64, i64, i64, i64]),
+        "sage_attention_ex": (ctypes.c_int, [p, p, p, i64, i64, i64, i64, i64, f32, ctypes.c_uint, p, p, p,
+                                             sz, p]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(L, name)
@@ -234,3 +244,101 @@ def sage_debug_qk_scores(q_i8, k_i8, B, S, H, b, h, r0, nr, c0, nc, D=128, score
     _check(lib().sage_debug_qk_scores(_ptr(q_i8), _ptr(k_i8), B, S, H, D, b, h, r0, nr, c0, nc,
                                       _ptr(scores), _stream_ptr(stream)))
     return scores
+
+
+def sage_k_smooth_scratch_bytes(B, S, H, D=128) -> int:
+    return lib().sage_k_smooth_scratch_bytes(B, S, H, D)
+
+
+def sage_workspace_bytes_ex(B, Sq, Skv, H, D=128) -> int:
+    return lib().sage_workspace_bytes_ex(B, Sq, Skv, H, D)
+
+
+def sage_quant_k_smooth(k, k_i8=None, k_scale=None, k_mean=None, scratch=None, stream=None):
+    """K smoothing + INT8 quantization. Returns (k_i8 [B,H,S_pad,D], k_scale [B,H,S_pad/32], k_mean [B,H,D])."""
+    torch = _torch()
+    _require(k, torch.bfloat16, "k")
+    B, S, H, D = _shape_bshd(k)
+    Sp = sage_seq_pad(S)
+    if k_i8 is None:
+        k_i8 = torch.empty((B, H, Sp, D), dtype=torch.int8, device=k.device)
+    if k_scale is None:
+        k_scale = torch.empty((B, H, Sp // 32), dtype=torch.float32, device=k.device)
+    if k_mean is None:
+        k_mean = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
+    nbytes = sage_k_smooth_scratch_bytes(B, S, H, D)
+    if scratch is None:
+        scratch = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=k.device)
+    _require(k_i8, torch.int8, "k_i8")
+    _require(k_scale, torch.float32, "k_scale")
+    _require(k_mean, torch.float32, "k_mean")
+    if k_i8.numel() < B * H * Sp * D or k_scale.numel() < B * H * (Sp // 32) or k_mean.numel() < B * H * D:
+        raise ValueError("output buffers too small")
+    _check(lib().sage_quant_k_smooth(_ptr(k), B, S, H, D, _ptr(k_i8), _ptr(k_scale), _ptr(k_mean), _ptr(scratch),
+                                     scratch.numel() * scratch.element_size(), _stream_ptr(stream)))
+    return k_i8, k_scale, k_mean
+
+
+def sage_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, Sq, Skv, H, D=128,
+                     softmax_scale=None, out=None, lse=None, return_lse=False, stream=None):
+    """Fused attention on quantized inputs with Sq queries and Skv keys.
+
+    Returns bf16 out [B, Sq, H, D], or (out, lse fp32 [B, H, Sq]) when ``lse``
+    is given or ``return_lse`` is set."""
+    torch = _torch()
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q_i8.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q_i8.device)
+    Sqp, Skp = sage_seq_pad(Sq), sage_seq_pad(Skv)
+    checks = [(q_i8, B * H * Sqp * D, torch.int8), (k_i8, B * H * Skp * D, torch.int8),
+              (v_fp8_t, B * H * D * Skp, torch.uint8), (q_scale, B * H * (Sqp // 32), torch.float32),
+              (k_scale, B * H * (Skp // 32), torch.float32), (v_scale, B * H * D, torch.float32),
+              (out, B * Sq * H * D, torch.bfloat16)]
+    if lse is not None:
+        checks.append((lse, B * H * Sq, torch.float32))
+    for t, n, dt in checks:
+        _require(t, dt, "tensor")
+        if t.numel() < n:
+            raise ValueError("buffer too small for the given sizes")
+    _check(lib().sage_attn_fwd_ex(_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v_fp8_t),
+                                  _ptr(v_scale), B, Sq, Skv, H, D, float(softmax_scale), _ptr(out), _ptr(lse),
+                                  _stream_ptr(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def sage_attention_ex(q, k, v, softmax_scale=None, flags=0, out=None, lse=None, return_lse=False,
+                      workspace=None, stream=None):
+    """Quantized attention for q [B, Sq, H, 128] and k, v [B, Skv, H, 128] (bf16).
+
+    ``flags`` may hold SAGE_SMOOTH_K. Returns out [B, Sq, H, 128], or
+    (out, lse [B, H, Sq]) when ``lse`` is given or ``return_lse`` is set."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, torch.bfloat16, n)
+    B, Sq, H, D = _shape_bshd(q)
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+        raise ValueError("k and v must be [B, Skv, H, D] with q's B, H and D")
+    Skv = int(k.shape[1])
+    if D != 128:
+        raise ValueError("head dim must be 128")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, torch.bfloat16, "out")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, torch.float32, "lse")
+        if lse.numel() < B * H * Sq:
+            raise ValueError("lse buffer too small")
+    nbytes = sage_workspace_bytes_ex(B, Sq, Skv, H, D)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check(lib().sage_attention_ex(_ptr(q), _ptr(k), _ptr(v), B, Sq, Skv, H, D, float(softmax_scale),
+                                   int(flags), _ptr(out), _ptr(lse), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    return (out, lse) if lse is not None else out

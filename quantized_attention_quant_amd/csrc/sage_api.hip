@@ -100,15 +100,42 @@ Workspace layout(int64_t B, int64_t S, int64_t H) {
 }
 
 sage_status quant_qk_impl(const void* x, int64_t B, int64_t S, int64_t H, int8_t* xq, float* xs,
-                          hipStream_t st) {
+                          hipStream_t st, const float* xmean = nullptr) {
   const int64_t Sp = seq_pad(S);
   const int nbp = (int)(Sp / sage::kQBlock);
   const int64_t total = B * H * nbp;
   const int64_t grid = (total + 3) / 4;
   if (grid > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
-  hipLaunchKernelGGL(sage::quant_qk_kernel, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)x,
-                     (int)S, (int)H, (int)Sp, nbp, total, xq, xs);
+  if (xmean)
+    hipLaunchKernelGGL(sage::quant_qk_kernel<true>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)x,
+                       (int)S, (int)H, (int)Sp, nbp, total, xmean, xq, xs);
+  else
+    hipLaunchKernelGGL(sage::quant_qk_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)x,
+                       (int)S, (int)H, (int)Sp, nbp, total, (const float*)nullptr, xq, xs);
   return launched("sage_quant_qk");
+}
+
+size_t k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H) {
+  // block sums [B*H, S_pad/32, 128]
+  return align256((size_t)(B * H * (seq_pad(S) / sage::kQBlock) * 128) * 4);
+}
+
+// K smoothing: per-channel mean over S, then INT8 quantization of K - mean.
+sage_status quant_k_smooth_impl(const void* k, int64_t B, int64_t S, int64_t H, int8_t* kq, float* ks,
+                                float* kmean, void* scratch, hipStream_t st) {
+  const int64_t Sp = seq_pad(S);
+  const int nbp = (int)(Sp / sage::kQBlock);
+  const int64_t total = B * H * nbp;
+  const int64_t grid = (total + 15) / 16;
+  const int64_t BH = B * H;
+  if (grid > INT32_MAX || BH > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
+  hipLaunchKernelGGL(sage::k_block_sum_kernel, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)k,
+                     (int)S, (int)H, nbp, total, (float*)scratch);
+  SAGE_TRY(launched("sage_quant_k_smooth (block sums)"));
+  hipLaunchKernelGGL(sage::k_mean_kernel, dim3((unsigned)BH), dim3(128), 0, st, (const float*)scratch, nbp,
+                     (int)S, kmean);
+  SAGE_TRY(launched("sage_quant_k_smooth (mean)"));
+  return quant_qk_impl(k, B, S, H, kq, ks, st, kmean);
 }
 
 sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, uint8_t* vt, float* vs,
@@ -133,17 +160,40 @@ sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, uint8_t
 }
 
 sage_status attn_impl(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
-                      const uint8_t* vt, const float* vs, int64_t B, int64_t S, int64_t H,
-                      float softmax_scale, void* out, hipStream_t st) {
-  const int64_t Sp = seq_pad(S);
-  const int nqt = (int)((S + sage::kQueryTile - 1) / sage::kQueryTile);
+                      const uint8_t* vt, const float* vs, int64_t B, int64_t Sq, int64_t Skv, int64_t H,
+                      float softmax_scale, void* out, float* lse, hipStream_t st) {
+  const int nqt = (int)((Sq + sage::kQueryTile - 1) / sage::kQueryTile);
   const int64_t nwg = B * H * nqt;
   if (nwg > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
   const float c = (float)softmax_scale * (float)1.4426950408889634;  // fl32(fl32(scale) * fl32(log2 e))
   const float log2_448 = (float)std::log2(448.0);
-  hipLaunchKernelGGL(sage::attn_fwd_kernel, dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st, q8, qs, k8, ks, vt, vs,
-                     (int)S, (int)H, (int)Sp, nqt, (int)nwg, c, log2_448, (uint16_t*)out);
+  hipLaunchKernelGGL(sage::attn_fwd_kernel, dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st, q8, qs, k8, ks,
+                     vt, vs, (int)Sq, (int)Skv, (int)H, (int)seq_pad(Sq), (int)seq_pad(Skv), nqt, (int)nwg, c,
+                     log2_448, (uint16_t*)out, lse);
   return launched("sage_attn_fwd");
+}
+
+struct WorkspaceEx {
+  size_t q8, k8, v8, qs, ks, vs, kmean, scratch, scratch_bytes, total;
+};
+
+// Intermediates of sage_attention_ex, each 256-byte aligned; the scratch
+// region serves sage_quant_v and, before it, the K-smoothing block sums.
+WorkspaceEx layout_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H) {
+  WorkspaceEx w{};
+  const int64_t Sqp = seq_pad(Sq), Skp = seq_pad(Skv);
+  w.q8 = 0;
+  w.k8 = w.q8 + align256((size_t)(B * H * Sqp * 128));
+  w.v8 = w.k8 + align256((size_t)(B * H * Skp * 128));
+  w.qs = w.v8 + align256((size_t)(B * H * Skp * 128));
+  w.ks = w.qs + align256((size_t)(B * H * (Sqp / 32)) * 4);
+  w.vs = w.ks + align256((size_t)(B * H * (Skp / 32)) * 4);
+  w.kmean = w.vs + align256((size_t)(B * H * 128) * 4);
+  w.scratch = w.kmean + align256((size_t)(B * H * 128) * 4);
+  const size_t a = v_scratch_bytes(B, Skv, H), b = k_smooth_scratch_bytes(B, Skv, H);
+  w.scratch_bytes = a > b ? a : b;
+  w.total = w.scratch + w.scratch_bytes;
+  return w;
 }
 
 }  // namespace
@@ -218,7 +268,7 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
   SAGE_TRY(check_ptr(out, "out"));
   if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, H, softmax_scale, out,
+  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, S, H, softmax_scale, out, nullptr,
                    (hipStream_t)stream);
 }
 
@@ -248,7 +298,7 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
   SAGE_TRY(quant_qk_impl(q, B, S, H, q8, qs, st));
   SAGE_TRY(quant_qk_impl(k, B, S, H, k8, ks, st));
   SAGE_TRY(quant_v_impl(v, B, S, H, v8, vs, ws + w.scratch, st));
-  return attn_impl(q8, qs, k8, ks, v8, vs, B, S, H, softmax_scale, out, st);
+  return attn_impl(q8, qs, k8, ks, v8, vs, B, S, S, H, softmax_scale, out, nullptr, st);
 }
 
 sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t B, int64_t S, int64_t H,
@@ -271,6 +321,85 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
                      q_i8, k_i8, (int)Sp, b * H + h, (int)rA, (int)r0, (int)nr, (int)cA, (int)c0, (int)nc,
                      scores);
   return launched("sage_debug_qk_scores");
+}
+
+size_t sage_k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
+  if (check_shape(B, S, H, D) != SAGE_OK) return 0;
+  return k_smooth_scratch_bytes(B, S, H);
+}
+
+sage_status sage_quant_k_smooth(const void* k, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* k_i8,
+                                float* k_scale, float* k_mean, void* scratch, size_t scratch_bytes,
+                                void* stream) {
+  SAGE_TRY(check_shape(B, S, H, D));
+  SAGE_TRY(check_ptr(k, "k"));
+  SAGE_TRY(check_ptr(k_i8, "k_i8"));
+  SAGE_TRY(check_ptr(k_scale, "k_scale"));
+  SAGE_TRY(check_ptr(k_mean, "k_mean"));
+  SAGE_TRY(check_ptr(scratch, "scratch"));
+  if (scratch_bytes < k_smooth_scratch_bytes(B, S, H))
+    return fail(SAGE_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, k_smooth_scratch_bytes(B, S, H));
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  return quant_k_smooth_impl(k, B, S, H, k_i8, k_scale, k_mean, scratch, (hipStream_t)stream);
+}
+
+sage_status sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                             const uint8_t* v_fp8_t, const float* v_scale, int64_t B, int64_t Sq, int64_t Skv,
+                             int64_t H, int64_t D, float softmax_scale, void* out, float* lse, void* stream) {
+  SAGE_TRY(check_shape(B, Sq, H, D));
+  SAGE_TRY(check_shape(B, Skv, H, D));
+  SAGE_TRY(check_ptr(q_i8, "q_i8"));
+  SAGE_TRY(check_ptr(q_scale, "q_scale"));
+  SAGE_TRY(check_ptr(k_i8, "k_i8"));
+  SAGE_TRY(check_ptr(k_scale, "k_scale"));
+  SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
+  SAGE_TRY(check_ptr(v_scale, "v_scale"));
+  SAGE_TRY(check_ptr(out, "out"));
+  if (lse && (((uintptr_t)lse) & 3)) return fail(SAGE_ERR_ALIGN, "lse is not 4-byte aligned");
+  if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, Sq, Skv, H, softmax_scale, out, lse,
+                   (hipStream_t)stream);
+}
+
+size_t sage_workspace_bytes_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D) {
+  if (check_shape(B, Sq, H, D) != SAGE_OK || check_shape(B, Skv, H, D) != SAGE_OK) return 0;
+  return layout_ex(B, Sq, Skv, H).total;
+}
+
+sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64_t B, int64_t Sq, int64_t Skv,
+                              int64_t H, int64_t D, float softmax_scale, unsigned flags, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  SAGE_TRY(check_shape(B, Sq, H, D));
+  SAGE_TRY(check_shape(B, Skv, H, D));
+  SAGE_TRY(check_ptr(q, "q"));
+  SAGE_TRY(check_ptr(k, "k"));
+  SAGE_TRY(check_ptr(v, "v"));
+  SAGE_TRY(check_ptr(out, "out"));
+  if (flags & ~(unsigned)SAGE_SMOOTH_K) return fail(SAGE_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (lse && (((uintptr_t)lse) & 3)) return fail(SAGE_ERR_ALIGN, "lse is not 4-byte aligned");
+  if (!workspace) return fail(SAGE_ERR_NULL, "workspace is NULL");
+  if (((uintptr_t)workspace) & 255) return fail(SAGE_ERR_ALIGN, "workspace is not 256-byte aligned");
+  const WorkspaceEx w = layout_ex(B, Sq, Skv, H);
+  if (workspace_bytes < w.total)
+    return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
+  if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  char* ws = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  int8_t* q8 = (int8_t*)(ws + w.q8);
+  int8_t* k8 = (int8_t*)(ws + w.k8);
+  uint8_t* v8 = (uint8_t*)(ws + w.v8);
+  float* qs = (float*)(ws + w.qs);
+  float* ks = (float*)(ws + w.ks);
+  float* vs = (float*)(ws + w.vs);
+  SAGE_TRY(quant_qk_impl(q, B, Sq, H, q8, qs, st));
+  if (flags & SAGE_SMOOTH_K)
+    SAGE_TRY(quant_k_smooth_impl(k, B, Skv, H, k8, ks, (float*)(ws + w.kmean), ws + w.scratch, st));
+  else
+    SAGE_TRY(quant_qk_impl(k, B, Skv, H, k8, ks, st));
+  SAGE_TRY(quant_v_impl(v, B, Skv, H, v8, vs, ws + w.scratch, st));
+  return attn_impl(q8, qs, k8, ks, v8, vs, B, Sq, Skv, H, softmax_scale, out, lse, st);
 }
 
 }  // extern "C"

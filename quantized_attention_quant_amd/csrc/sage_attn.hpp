@@ -266,9 +266,9 @@ __device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qscale,
                      const int8_t* __restrict__ k8, const float* __restrict__ kscale,
-                     const uint8_t* __restrict__ v8t, const float* __restrict__ vscale, int S, int H,
-                     int S_pad, int nqt, int num_wg, float c, float log2_448,
-                     uint16_t* __restrict__ out) {
+                     const uint8_t* __restrict__ v8t, const float* __restrict__ vscale, int Sq, int Skv,
+                     int H, int Sq_pad, int Skv_pad, int nqt, int num_wg, float c, float log2_448,
+                     uint16_t* __restrict__ out, float* __restrict__ lse) {
   static_assert(kAttnWaves == 8, "the phase skew pairs waves w and w + 4");
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k[3][kKeyTile * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_v[3][kKeyTile * 128];
@@ -281,13 +281,11 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const bool lead = wave_s < 4;
   const int q0 = qt * kQueryTile + wave * 32;
-  const int nbp = S_pad / kQBlock;
 
-  const uint8_t* kbase = (const uint8_t*)k8 + bh * S_pad * kHeadDim;
-  const uint8_t* vbase = v8t + bh * kHeadDim * (int64_t)S_pad;
-  const float* ksb = kscale + bh * nbp;
-  const int T = (S + kKeyTile - 1) / kKeyTile;
-  const bool ragged = (S % kKeyTile) != 0;
+  const uint8_t* kbase = (const uint8_t*)k8 + bh * Skv_pad * kHeadDim;
+  const uint8_t* vbase = v8t + bh * kHeadDim * (int64_t)Skv_pad;
+  const float* ksb = kscale + bh * (Skv_pad / kQBlock);
+  const int T = (Skv + kKeyTile - 1) / kKeyTile;
 
   // Tiles stream into LDS with buffer_load ... lds: lane l of a wave
   // instruction writes LDS bytes [16 l, 16 l + 16) of an 8-row group, i.e.
@@ -296,7 +294,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   // a scalar. Buffer descriptors cover this head's K rows and V^T rows
   // (base, stride 0, size in bytes < 2^31, default data format).
   const uint64_t kaddr = (uint64_t)(uintptr_t)kbase, vaddr = (uint64_t)(uintptr_t)vbase;
-  const uint32_t nbytes = (uint32_t)S_pad * kHeadDim;
+  const uint32_t nbytes = (uint32_t)Skv_pad * kHeadDim;
   const v4i rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)kaddr),
                   __builtin_amdgcn_readfirstlane((int)(uint32_t)(kaddr >> 32) & 0xFFFF),
                   __builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000};
@@ -309,7 +307,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
     const int row = 8 * (wave + 8 * i) + (lane >> 3);
     const int chunk = ((lane & 7) ^ swz_key(row)) << 4;
     koff[i] = (uint32_t)(row * kHeadDim + chunk);
-    voff[i] = (uint32_t)(row * S_pad + chunk);
+    voff[i] = (uint32_t)(row * Skv_pad + chunk);
   }
   // LDS byte address of the first 1 KB row group this wave writes per slot.
   const uint32_t kl0 = lds_addr(lds_k[0]) + wave_s * 1024, vl0 = lds_addr(lds_v[0]) + wave_s * 1024;
@@ -329,8 +327,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   if (T > 1) load_k(1, 1);
 
   v4i qf[4];
-  load_q_frag(q8 + ((bh * S_pad + q0 + li) * kHeadDim + 64 * g), qf);
-  const float qs = qscale[bh * nbp + q0 / kQBlock];
+  load_q_frag(q8 + ((bh * Sq_pad + q0 + li) * kHeadDim + 64 * g), qf);
+  const float qs = qscale[bh * (Sq_pad / kQBlock) + q0 / kQBlock];
 
   v16i bias;
 #pragma unroll
@@ -348,7 +346,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   // The two wave groups run separate loops with the same barrier count:
   // interval i (0 <= i < T-1) ends with a barrier; tile i lives in slot
   // i % 3 of both rings. The last interval (i = T-1), whose tile may be
-  // ragged (keys >= S masked), has no barrier after it.
+  // ragged (keys >= Skv masked), has no barrier after it.
   if (lead) {
     qk_tile(lds_k[0], qf, li, g, bias, s);
     for (int i = 0; i < T - 1; ++i) {
@@ -362,7 +360,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
       __syncthreads();
     }
     const int i = T - 1;
-    vector_phase<true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, S - i * kKeyTile, g, st, o, pop);
+    vector_phase<true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
     pv_tile(lds_v[i % 3], pop, li, g, o);
   } else {
     for (int i = 0; i < T - 1; ++i) {
@@ -379,18 +377,24 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
     const int sl = i % 3;
     if (i > 0) pv_tile(lds_v[(sl + 2) % 3], pop, li, g, o);
     qk_tile(lds_k[sl], qf, li, g, bias, s);
-    vector_phase<true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, S - i * kKeyTile, g, st, o, pop);
+    vector_phase<true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
     pv_tile(lds_v[sl], pop, li, g, o);
   }
 
-  // Epilogue: O = acc * v_scale / l, bf16, layout [B, S, H, D].
+  // Epilogue: O = acc * v_scale / l, bf16, layout [B, Sq, H, D]; optional
+  // log-sum-exp [B, H, Sq].
   const float lt = pair_sum(st.l);
   const float rl = __fdiv_rn(1.0f, lt);
   const int qi = q0 + li;
-  if (qi < S) {
+  if (lse != nullptr && g == 0 && qi < Sq) {
+    // log-sum-exp of the row's scaled scores: l = sum 2^(t - m2), so
+    // ln sum e^(scale * score) = ln 2 * (m2 + log2 l)
+    lse[bh * Sq + qi] = (st.m2 + __builtin_amdgcn_logf(lt)) * 0.6931471805599453f;
+  }
+  if (qi < Sq) {
     const int h = (int)(bh % H);
     const int64_t b = bh / H;
-    uint16_t* orow = out + ((b * S + qi) * H + h) * kHeadDim;
+    uint16_t* orow = out + ((b * Sq + qi) * H + h) * kHeadDim;
     const float* vsb = vscale + bh * kHeadDim;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {

@@ -13,8 +13,12 @@ namespace sage {
 
 // One wave per (b, h, 32-row block); 4 waves per workgroup.
 // Lane l covers columns [8 (l%16), +8) of rows 4 it + l/16, it = 0..7.
+// kSmooth: the values quantized are fl32(x - xmean[b, h, c]) (K smoothing);
+// rows >= S stay zero.
+template <bool kSmooth>
 __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restrict__ x, int S, int H,
                                                        int S_pad, int nbp, int64_t total_blocks,
+                                                       const float* __restrict__ xmean,
                                                        int8_t* __restrict__ xq,
                                                        float* __restrict__ xscale) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -27,6 +31,11 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
   const int col = (lane & 15) * 8;
   const int r0 = t * kQBlock;
 
+  float mu[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (kSmooth) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mu[j] = xmean[bh * kHeadDim + col + j];
+  }
   float v[8][8];
   float amax = 0.0f;
 #pragma unroll
@@ -39,8 +48,13 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
     for (int j = 0; j < 4; ++j) {
       v[it][2 * j] = bf16_to_f32(ws[j] & 0xFFFFu);
       v[it][2 * j + 1] = bf16_to_f32(ws[j] >> 16);
-      amax = fmaxf(amax, fmaxf(fabsf(v[it][2 * j]), fabsf(v[it][2 * j + 1])));
     }
+    if (kSmooth && row < S) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[it][j] = v[it][j] - mu[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[it][j]));
   }
   amax = wave_max(amax);
   float scale = 0.0f, inv = 0.0f;
@@ -159,6 +173,49 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     *(uint4*)(dst + 16 * q) = *(const uint4*)(&tile[c][64 * half + 16 * q]);
+}
+
+// K smoothing, step 1: per (b, h, 32-row block) fp32 sum of each channel,
+// rows added one at a time in increasing s (rows >= S contribute nothing).
+// Four blocks per wave: lane l covers channels [8 (l%16), +8) of block
+// 4 (4 blockIdx + wave) + l/16.
+__global__ __launch_bounds__(256) void k_block_sum_kernel(const uint16_t* __restrict__ k, int S, int H,
+                                                          int nbp, int64_t total_blocks,
+                                                          float* __restrict__ partial) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t blk = ((int64_t)blockIdx.x * 4 + wave) * 4 + (lane >> 4);
+  if (blk >= total_blocks) return;
+  const int t = (int)(blk % nbp);
+  const int64_t bh = blk / nbp;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const int col = (lane & 15) * 8;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int rend = min(S, (t + 1) * kQBlock);
+  for (int row = t * kQBlock; row < rend; ++row) {
+    const uint4 w = *(const uint4*)(k + (((b * S + row) * H + h) * kHeadDim + col));
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = acc[2 * j] + bf16_to_f32(ws[j] & 0xFFFFu);
+      acc[2 * j + 1] = acc[2 * j + 1] + bf16_to_f32(ws[j] >> 16);
+    }
+  }
+  float4* dst = (float4*)(partial + blk * kHeadDim + col);
+  dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+// K smoothing, step 2: the block sums added in block order, then
+// mean = fl32(sum / S). grid B*H, 128 threads (one per channel).
+__global__ __launch_bounds__(128) void k_mean_kernel(const float* __restrict__ partial, int nbp, int S,
+                                                     float* __restrict__ kmean) {
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x;
+  const float* p = partial + bh * (int64_t)nbp * kHeadDim + c;
+  float sum = 0.0f;
+  for (int t = 0; t < nbp; ++t) sum = sum + p[(int64_t)t * kHeadDim];
+  kmean[bh * kHeadDim + c] = __fdiv_rn(sum, (float)S);
 }
 
 }  // namespace sage

@@ -30,7 +30,9 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ("sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attention", "sage_debug_qk_scores",
-              "sage_workspace_bytes", "sage_kv_tile", "sage_seq_pad"):
+              "sage_workspace_bytes", "sage_kv_tile", "sage_seq_pad", "sage_quant_k_smooth",
+              "sage_k_smooth_scratch_bytes", "sage_attn_fwd_ex", "sage_workspace_bytes_ex",
+              "sage_attention_ex"):
         assert n in names
 
 
@@ -94,6 +96,42 @@ def test_validation_codes():
     assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 128, 0, 0, 0, 0, 0, 1, f, z) == ERR_RANGE
 
 
+def test_extended_entry_points_validation():
+    p = ctypes.c_void_p
+    f, m, z = p(FAKE), p(MISALIGNED), p(0)
+    fl = ctypes.c_float(0.1)
+    # workspace for cross-attention covers both lengths and the smoothing scratch
+    for B, Sq, Skv, H in ((1, 300, 77, 2), (1, 64, 4096, 24), (2, 75600, 75600, 40)):
+        ws = sage.sage_workspace_bytes_ex(B, Sq, Skv, H, 128)
+        Sqp, Skp = sage.sage_seq_pad(Sq), sage.sage_seq_pad(Skv)
+        base = B * H * 128 * (Sqp + 2 * Skp)
+        assert base <= ws <= base * 1.15 + 65536   # + block sums of K smoothing (16 B per key row)
+        if Sq == Skv:
+            assert ws >= sage.sage_workspace_bytes(B, Sq, H, 128)
+    assert sage.sage_workspace_bytes_ex(1, 300, 0, 2, 128) == 0
+    assert sage.sage_workspace_bytes_ex(1, 300, 77, 2, 64) == 0
+    nb = sage.sage_k_smooth_scratch_bytes(1, 300, 2, 128)
+    assert nb >= 2 * (sage.sage_seq_pad(300) // 32) * 128 * 4
+    # sage_quant_k_smooth
+    assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, f, f, f, f, nb - 1, z) == ERR_WS
+    assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, f, f, z, f, nb, z) == ERR_NULL
+    assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, m, f, f, f, nb, z) == ERR_ALIGN
+    assert _call("sage_quant_k_smooth", f, 1, 300, 2, 96, f, f, f, f, nb, z) == ERR_UNSUP
+    # sage_attn_fwd_ex: both lengths are checked, lse alignment is checked
+    args = [f, f, f, f, f, f]
+    assert _call("sage_attn_fwd_ex", *args, 1, 300, 0, 2, 128, fl, f, z, z) == ERR_SHAPE
+    assert _call("sage_attn_fwd_ex", *args, 1, 0, 77, 2, 128, fl, f, z, z) == ERR_SHAPE
+    assert _call("sage_attn_fwd_ex", *args, 1, 300, 77, 2, 128, fl, f, p(FAKE + 2), z) == ERR_ALIGN
+    assert _call("sage_attn_fwd_ex", *args, 1, 300, 77, 2, 128, ctypes.c_float(float("inf")), f, z, z) == ERR_SHAPE
+    assert _call("sage_attn_fwd_ex", f, f, f, f, f, f, 1, 300, 77, 2, 128, fl, z, z, z) == ERR_NULL
+    # sage_attention_ex: flags, workspace
+    ws = sage.sage_workspace_bytes_ex(1, 300, 77, 2, 128)
+    assert _call("sage_attention_ex", f, f, f, 1, 300, 77, 2, 128, fl, 2, f, z, f, ws, z) == ERR_UNSUP
+    assert _call("sage_attention_ex", f, f, f, 1, 300, 77, 2, 128, fl, 1, f, z, f, ws - 1, z) == ERR_WS
+    assert _call("sage_attention_ex", f, f, f, 1, 300, 77, 2, 128, fl, 1, f, z, z, ws, z) == ERR_NULL
+    assert _call("sage_attention_ex", f, f, f, 1, 300, 77, 2, 128, fl, 0, f, z, p(FAKE + 64), ws, z) == ERR_ALIGN
+
+
 def test_forced_launch_failure_hook(monkeypatch):
     monkeypatch.setenv("SAGE_TEST_FAIL_LAUNCH", "1")
     p = ctypes.c_void_p
@@ -102,6 +140,11 @@ def test_forced_launch_failure_hook(monkeypatch):
     ws = sage.sage_workspace_bytes(1, 256, 2)
     assert _call("sage_attention", f, f, f, 1, 256, 2, 128, ctypes.c_float(0.1), f, f, ws, z) == ERR_HIP
     assert b"forced" in sage.lib().sage_last_error()
+    wsx = sage.sage_workspace_bytes_ex(1, 300, 77, 2, 128)
+    assert _call("sage_attention_ex", f, f, f, 1, 300, 77, 2, 128, ctypes.c_float(0.1), 1, f, f, f, wsx, z) == ERR_HIP
+    nb = sage.sage_k_smooth_scratch_bytes(1, 300, 2, 128)
+    assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, f, f, f, f, nb, z) == ERR_HIP
+    assert _call("sage_attn_fwd_ex", f, f, f, f, f, f, 1, 300, 77, 2, 128, ctypes.c_float(0.1), f, f, z) == ERR_HIP
     # validation still runs first
     assert _call("sage_quant_qk", f, 1, 256, 2, 64, f, f, z) == ERR_UNSUP
 
