@@ -260,7 +260,9 @@ __device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int
 //   interval i, waves 0-3: softmax(i), PV(i), QK(i+1)
 //   interval i, waves 4-7: PV(i-1), QK(i), softmax(i)
 // (waves 0-3 compute QK(0) before interval 0; waves 4-7 compute PV(T-1)
-// after the last one). Interval i reads K tiles i, i+1 and V tiles i-1, i,
+// after the last one). The matrix phase runs at raised wave priority
+// (s_setprio 2): its few MFMA and LDS issues then go first, and the other
+// wave's vector work fills the cycles between them. Interval i reads K tiles i, i+1 and V tiles i-1, i,
 // and loads K tile i+2 and V tile i+1 into the third slot of each
 // three-stage LDS ring.
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2)))
@@ -354,8 +356,10 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
       if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
       load_v(i + 1, (sl + 1) % 3);
       vector_phase<false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
+      __builtin_amdgcn_s_setprio(2);
       pv_tile(lds_v[sl], pop, li, g, o);
       qk_tile(lds_k[(sl + 1) % 3], qf, li, g, bias, s);
+      __builtin_amdgcn_s_setprio(0);
       wait_tiles();
       __syncthreads();
     }
@@ -367,8 +371,10 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
       const int sl = i % 3;
       if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
       load_v(i + 1, (sl + 1) % 3);
+      __builtin_amdgcn_s_setprio(2);
       if (i > 0) pv_tile(lds_v[(sl + 2) % 3], pop, li, g, o);
       qk_tile(lds_k[sl], qf, li, g, bias, s);
+      __builtin_amdgcn_s_setprio(0);
       vector_phase<false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
       wait_tiles();
       __syncthreads();

@@ -135,7 +135,12 @@ __global__ __launch_bounds__(128) void v_scale_kernel(const float* __restrict__ 
 
 // Quantize 128 keys x 128 channels of V to E4M3FN and write them transposed
 // ([channel][key]) with keys permuted inside each 64-key group.
-// grid (S_pad/128, B*H), 256 threads.
+// grid (S_pad/128, B*H), 256 threads. Thread t covers channels
+// [8 (t/16), +8) of 8 keys that land in 8 consecutive slots: within a 32-key
+// block u of a 64-key group, key 32u + 4m + e (m = 0..7, e = 0..3) goes to
+// slot 32 (m%2) + 16u + 4 (m/2) + e, so quads m = g + 4pr and g + 4pr + 2
+// fill slots [32g + 16u + 8pr, +8). The 16 threads of a channel group write
+// one 128-byte row of the LDS tile between them.
 __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict__ v, int S, int H,
                                                       int S_pad, const float* __restrict__ vinv,
                                                       uint8_t* __restrict__ vt) {
@@ -144,28 +149,33 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
-  const int cg = threadIdx.x & 15, ro = threadIdx.x >> 4;
+  const int run = threadIdx.x & 15, cg = threadIdx.x >> 4;
+  const int grp = run >> 3, u = (run >> 2) & 1, g = (run >> 1) & 1, pr = run & 1;
+  const int kq0 = 64 * grp + 32 * u + 4 * (g + 4 * pr);   // first key of quad m0; quad m1 is 8 keys later
+  const int slot = 64 * grp + 32 * g + 16 * u + 8 * pr;
   float inv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) inv[j] = vinv[bh * kHeadDim + cg * 8 + j];
+  float y[8][8];   // [key][channel]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int kk = ro + 16 * i;  // key within the 128-key tile
-    const int row = k0 + kk;
+  for (int e = 0; e < 8; ++e) {
+    const int row = k0 + kq0 + (e & 3) + 8 * (e >> 2);
     uint4 w = make_uint4(0, 0, 0, 0);
     if (row < S) w = *(const uint4*)(v + (((b * S + row) * H + h) * kHeadDim + cg * 8));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    const int slot = (kk & ~(kVGroup - 1)) | vslot_of_key(kk & (kVGroup - 1));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float y0 = bf16_to_f32(ws[j] & 0xFFFFu) * inv[2 * j];
-      float y1 = bf16_to_f32(ws[j] >> 16) * inv[2 * j + 1];
-      y0 = fminf(fmaxf(y0, -448.0f), 448.0f);
-      y1 = fminf(fmaxf(y1, -448.0f), 448.0f);
-      const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-      tile[cg * 8 + 2 * j][slot] = (uint8_t)(pk & 0xFFu);
-      tile[cg * 8 + 2 * j + 1][slot] = (uint8_t)((pk >> 8) & 0xFFu);
+      y[e][2 * j] = fminf(fmaxf(bf16_to_f32(ws[j] & 0xFFFFu) * inv[2 * j], -448.0f), 448.0f);
+      y[e][2 * j + 1] = fminf(fmaxf(bf16_to_f32(ws[j] >> 16) * inv[2 * j + 1], -448.0f), 448.0f);
     }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0][j], y[1][j], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2][j], y[3][j], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4][j], y[5][j], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6][j], y[7][j], hi, true);
+    *(uint2*)(&tile[cg * 8 + j][slot]) = make_uint2((uint32_t)lo, (uint32_t)hi);
   }
   __syncthreads();
   const int c = threadIdx.x >> 1, half = threadIdx.x & 1;
