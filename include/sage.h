@@ -26,8 +26,13 @@
  *   - No global mutable state besides that string: calls are thread-safe;
  *     calls that share output or workspace buffers must be ordered by the
  *     caller.
- *   - Sizes: B, S, H >= 1, D == 128, S <= 2^24, B, H <= 2^20 and
- *     B*H*S_pad*128 < 2^62; larger sizes return SAGE_ERR_SHAPE.
+ *   - Sizes: B, S, H >= 1, S <= 2^24, B, H <= 2^20 and B*H*S_pad*D < 2^62;
+ *     larger sizes return SAGE_ERR_SHAPE.
+ *   - Head dim: D == 128 is the pages' operation. D == 64 is also accepted
+ *     by every entry point except sage_debug_qk_scores (the pages' callers
+ *     fall back for it: the VAE's head dim 64, diffusers PR #15060, section
+ *     "What does this PR do?"); every "128" channel count below then reads
+ *     D. Other head dims return SAGE_ERR_UNSUPPORTED.
  *   - Inputs containing NaN/Inf, or whose scaled scores overflow fp32, are
  *     outside the contract (no guarantee on the output).
  */
@@ -45,7 +50,7 @@ typedef enum {
   SAGE_OK = 0,
   SAGE_ERR_NULL = 1,        /* a required pointer is NULL                     */
   SAGE_ERR_SHAPE = 2,       /* B, S or H < 1, or sizes overflow               */
-  SAGE_ERR_UNSUPPORTED = 3, /* D != 128 (the only head size of the method)    */
+  SAGE_ERR_UNSUPPORTED = 3, /* head dim other than 128 or 64; unknown flags    */
   SAGE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
   SAGE_ERR_WORKSPACE = 5,   /* workspace/scratch smaller than required        */
   SAGE_ERR_HIP = 6,         /* a HIP launch failed                            */
@@ -155,6 +160,7 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
  * INT8 MFMA operand loading and instruction sequence as sage_attn_fwd.
  *   scores  int32 [nr, nc] out, row-major.
  * Windows must satisfy 0 <= r0, 0 < nr, r0+nr <= S_pad (same for keys).
+ * D must be 128 (SAGE_ERR_UNSUPPORTED otherwise).
  */
 sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t B, int64_t S,
                                  int64_t H, int64_t D, int64_t b, int64_t h, int64_t r0,

@@ -210,15 +210,15 @@ def sage_attn_fwd(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, H, D=128
 
 
 def sage_attention(q, k, v, softmax_scale=None, out=None, workspace=None, stream=None):
-    """gfx1201_sage_attention(q, k, v, softmax_scale) on MI355X: bf16 [B, S, H, 128] -> same."""
+    """gfx1201_sage_attention(q, k, v, softmax_scale) on MI355X: bf16 [B, S, H, D] -> same (D = 128, or 64)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, torch.bfloat16, n)
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k and v must have the same shape")
     B, S, H, D = _shape_bshd(q)
-    if D != 128:
-        raise ValueError("head dim must be 128")
+    if D not in (64, 128):
+        raise ValueError("head dim must be 64 or 128")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -311,7 +311,7 @@ def sage_attn_fwd_ex(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, Sq, Skv,
 
 def sage_attention_ex(q, k, v, softmax_scale=None, flags=0, out=None, lse=None, return_lse=False,
                       workspace=None, stream=None):
-    """Quantized attention for q [B, Sq, H, 128] and k, v [B, Skv, H, 128] (bf16).
+    """Quantized attention for q [B, Sq, H, D] and k, v [B, Skv, H, D] (bf16, D = 64 or 128).
 
     ``flags`` may hold SAGE_SMOOTH_K. Returns out [B, Sq, H, 128], or
     (out, lse [B, H, Sq]) when ``lse`` is given or ``return_lse`` is set."""
@@ -322,8 +322,8 @@ def sage_attention_ex(q, k, v, softmax_scale=None, flags=0, out=None, lse=None, 
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
         raise ValueError("k and v must be [B, Skv, H, D] with q's B, H and D")
     Skv = int(k.shape[1])
-    if D != 128:
-        raise ValueError("head dim must be 128")
+    if D not in (64, 128):
+        raise ValueError("head dim must be 64 or 128")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
     if out is None:

@@ -38,7 +38,7 @@ bool forced_launch_failure() {
 int64_t seq_pad(int64_t S) { return (S + sage::kSeqAlign - 1) / sage::kSeqAlign * sage::kSeqAlign; }
 
 sage_status check_shape(int64_t B, int64_t S, int64_t H, int64_t D) {
-  if (D != sage::kHeadDim) return fail(SAGE_ERR_UNSUPPORTED, "head dim %lld unsupported (only 128)", (long long)D);
+  if (D != 128 && D != 64) return fail(SAGE_ERR_UNSUPPORTED, "head dim %lld unsupported (64 or 128)", (long long)D);
   if (B < 1 || S < 1 || H < 1) return fail(SAGE_ERR_SHAPE, "B, S, H must be >= 1 (got %lld, %lld, %lld)",
                                            (long long)B, (long long)S, (long long)H);
   // S_pad * B * H * D must stay well inside int64, and one head's quantized
@@ -46,7 +46,7 @@ sage_status check_shape(int64_t B, int64_t S, int64_t H, int64_t D) {
   // descriptor offset
   if (S > (int64_t)1 << 24 || B > (int64_t)1 << 20 || H > (int64_t)1 << 20)
     return fail(SAGE_ERR_SHAPE, "sizes too large (S <= 2^24, B, H <= 2^20)");
-  const double n = (double)B * (double)H * (double)seq_pad(S) * 128.0;
+  const double n = (double)B * (double)H * (double)seq_pad(S) * (double)D;
   if (n >= 4.0e18) return fail(SAGE_ERR_SHAPE, "sizes overflow");
   return SAGE_OK;
 }
@@ -73,19 +73,19 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t v_nchunk(int64_t S) { return (S + sage::kVChunkRows - 1) / sage::kVChunkRows; }
 
-size_t v_scratch_bytes(int64_t B, int64_t S, int64_t H) {
-  // partial maxima [B*H, nchunk, 128] + reciprocals [B*H, 128]
-  return align256((size_t)(B * H * v_nchunk(S) * 128) * 4) + align256((size_t)(B * H * 128) * 4);
+size_t v_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
+  // partial maxima [B*H, nchunk, D] + reciprocals [B*H, D]
+  return align256((size_t)(B * H * v_nchunk(S) * D) * 4) + align256((size_t)(B * H * D) * 4);
 }
 
 struct Workspace {
   size_t q8, k8, v8, qs, ks, vs, scratch, total, scratch_bytes;
 };
 
-Workspace layout(int64_t B, int64_t S, int64_t H) {
+Workspace layout(int64_t B, int64_t S, int64_t H, int64_t D) {
   Workspace w{};
   const int64_t Sp = seq_pad(S);
-  const size_t qk = align256((size_t)(B * H * Sp * 128));
+  const size_t qk = align256((size_t)(B * H * Sp * D));
   const size_t sc = align256((size_t)(B * H * (Sp / 32)) * 4);
   w.q8 = 0;
   w.k8 = w.q8 + qk;
@@ -93,83 +93,107 @@ Workspace layout(int64_t B, int64_t S, int64_t H) {
   w.qs = w.v8 + qk;
   w.ks = w.qs + sc;
   w.vs = w.ks + sc;
-  w.scratch = w.vs + align256((size_t)(B * H * 128) * 4);
-  w.scratch_bytes = v_scratch_bytes(B, S, H);
+  w.scratch = w.vs + align256((size_t)(B * H * D) * 4);
+  w.scratch_bytes = v_scratch_bytes(B, S, H, D);
   w.total = w.scratch + w.scratch_bytes;
   return w;
 }
 
-sage_status quant_qk_impl(const void* x, int64_t B, int64_t S, int64_t H, int8_t* xq, float* xs,
+template <int kD, bool kSmooth>
+void launch_quant_qk(const void* x, int64_t S, int64_t H, int64_t Sp, int nbp, int64_t total, int64_t grid,
+                     const float* xmean, int8_t* xq, float* xs, hipStream_t st) {
+  hipLaunchKernelGGL((sage::quant_qk_kernel<kD, kSmooth>), dim3((unsigned)grid), dim3(256), 0, st,
+                     (const uint16_t*)x, (int)S, (int)H, (int)Sp, nbp, total, xmean, xq, xs);
+}
+
+sage_status quant_qk_impl(const void* x, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* xq, float* xs,
                           hipStream_t st, const float* xmean = nullptr) {
   const int64_t Sp = seq_pad(S);
   const int nbp = (int)(Sp / sage::kQBlock);
   const int64_t total = B * H * nbp;
   const int64_t grid = (total + 3) / 4;
   if (grid > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
-  if (xmean)
-    hipLaunchKernelGGL(sage::quant_qk_kernel<true>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)x,
-                       (int)S, (int)H, (int)Sp, nbp, total, xmean, xq, xs);
-  else
-    hipLaunchKernelGGL(sage::quant_qk_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)x,
-                       (int)S, (int)H, (int)Sp, nbp, total, (const float*)nullptr, xq, xs);
+  if (D == 64) {
+    if (xmean) launch_quant_qk<64, true>(x, S, H, Sp, nbp, total, grid, xmean, xq, xs, st);
+    else launch_quant_qk<64, false>(x, S, H, Sp, nbp, total, grid, nullptr, xq, xs, st);
+  } else {
+    if (xmean) launch_quant_qk<128, true>(x, S, H, Sp, nbp, total, grid, xmean, xq, xs, st);
+    else launch_quant_qk<128, false>(x, S, H, Sp, nbp, total, grid, nullptr, xq, xs, st);
+  }
   return launched("sage_quant_qk");
 }
 
-size_t k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H) {
-  // block sums [B*H, S_pad/32, 128]
-  return align256((size_t)(B * H * (seq_pad(S) / sage::kQBlock) * 128) * 4);
+size_t k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
+  // block sums [B*H, S_pad/32, D]
+  return align256((size_t)(B * H * (seq_pad(S) / sage::kQBlock) * D) * 4);
 }
 
 // K smoothing: per-channel mean over S, then INT8 quantization of K - mean.
-sage_status quant_k_smooth_impl(const void* k, int64_t B, int64_t S, int64_t H, int8_t* kq, float* ks,
-                                float* kmean, void* scratch, hipStream_t st) {
+template <int kD>
+void launch_k_mean(const void* k, int64_t S, int64_t H, int nbp, int64_t total, int64_t BH, void* scratch,
+                   float* kmean, hipStream_t st) {
+  // 4 waves of 64/(kD/8) blocks each per workgroup
+  const int64_t per_wg = 4 * (64 / (kD / 8));
+  hipLaunchKernelGGL(sage::k_block_sum_kernel<kD>, dim3((unsigned)((total + per_wg - 1) / per_wg)), dim3(256), 0,
+                     st, (const uint16_t*)k, (int)S, (int)H, nbp, total, (float*)scratch);
+  hipLaunchKernelGGL(sage::k_mean_kernel<kD>, dim3((unsigned)BH), dim3(kD), 0, st, (const float*)scratch, nbp,
+                     (int)S, kmean);
+}
+
+sage_status quant_k_smooth_impl(const void* k, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* kq,
+                                float* ks, float* kmean, void* scratch, hipStream_t st) {
   const int64_t Sp = seq_pad(S);
   const int nbp = (int)(Sp / sage::kQBlock);
   const int64_t total = B * H * nbp;
-  const int64_t grid = (total + 15) / 16;
   const int64_t BH = B * H;
-  if (grid > INT32_MAX || BH > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
-  hipLaunchKernelGGL(sage::k_block_sum_kernel, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)k,
-                     (int)S, (int)H, nbp, total, (float*)scratch);
-  SAGE_TRY(launched("sage_quant_k_smooth (block sums)"));
-  hipLaunchKernelGGL(sage::k_mean_kernel, dim3((unsigned)BH), dim3(128), 0, st, (const float*)scratch, nbp,
-                     (int)S, kmean);
+  if ((total + 15) / 16 > INT32_MAX || BH > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
+  if (D == 64) launch_k_mean<64>(k, S, H, nbp, total, BH, scratch, kmean, st);
+  else launch_k_mean<128>(k, S, H, nbp, total, BH, scratch, kmean, st);
   SAGE_TRY(launched("sage_quant_k_smooth (mean)"));
-  return quant_qk_impl(k, B, S, H, kq, ks, st, kmean);
+  return quant_qk_impl(k, B, S, H, D, kq, ks, st, kmean);
 }
 
-sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, uint8_t* vt, float* vs,
+template <int kD>
+void launch_quant_v(const void* v, int64_t S, int64_t H, int64_t Sp, int nchunk, int64_t BH, float* partial,
+                    float* vinv, float* vs, uint8_t* vt, hipStream_t st) {
+  hipLaunchKernelGGL(sage::v_amax_partial_kernel<kD>, dim3(nchunk, (unsigned)BH), dim3(256), 0, st,
+                     (const uint16_t*)v, (int)S, (int)H, nchunk, partial);
+  hipLaunchKernelGGL(sage::v_scale_kernel<kD>, dim3((unsigned)BH), dim3(kD), 0, st, (const float*)partial, nchunk,
+                     vs, vinv);
+  hipLaunchKernelGGL(sage::v_quant_kernel<kD>, dim3((unsigned)(Sp / 128), (unsigned)BH), dim3(2 * kD), 0, st,
+                     (const uint16_t*)v, (int)S, (int)H, (int)Sp, (const float*)vinv, vt);
+}
+
+sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, int64_t D, uint8_t* vt, float* vs,
                          void* scratch, hipStream_t st) {
   const int64_t Sp = seq_pad(S);
   const int nchunk = (int)v_nchunk(S);
   const int64_t BH = B * H;
-  if (BH > 65535 * 1024LL) return fail(SAGE_ERR_SHAPE, "B*H too large");
-  float* partial = (float*)scratch;
-  float* vinv = (float*)((char*)scratch + align256((size_t)(BH * nchunk * 128) * 4));
-  // B*H goes in grid.y (limit 65535 on HIP): fold larger products into x.
+  // B*H goes in grid.y (limit 65535 on HIP)
   if (BH > 65535) return fail(SAGE_ERR_SHAPE, "B*H above 65535 unsupported");
-  hipLaunchKernelGGL(sage::v_amax_partial_kernel, dim3(nchunk, (unsigned)BH), dim3(256), 0, st,
-                     (const uint16_t*)v, (int)S, (int)H, nchunk, partial);
-  SAGE_TRY(launched("sage_quant_v (amax)"));
-  hipLaunchKernelGGL(sage::v_scale_kernel, dim3((unsigned)BH), dim3(128), 0, st, (const float*)partial,
-                     nchunk, vs, vinv);
-  SAGE_TRY(launched("sage_quant_v (scale)"));
-  hipLaunchKernelGGL(sage::v_quant_kernel, dim3((unsigned)(Sp / 128), (unsigned)BH), dim3(256), 0, st,
-                     (const uint16_t*)v, (int)S, (int)H, (int)Sp, (const float*)vinv, vt);
-  return launched("sage_quant_v (quantize)");
+  float* partial = (float*)scratch;
+  float* vinv = (float*)((char*)scratch + align256((size_t)(BH * nchunk * D) * 4));
+  if (D == 64) launch_quant_v<64>(v, S, H, Sp, nchunk, BH, partial, vinv, vs, vt, st);
+  else launch_quant_v<128>(v, S, H, Sp, nchunk, BH, partial, vinv, vs, vt, st);
+  return launched("sage_quant_v");
 }
 
 sage_status attn_impl(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
-                      const uint8_t* vt, const float* vs, int64_t B, int64_t Sq, int64_t Skv, int64_t H,
+                      const uint8_t* vt, const float* vs, int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
                       float softmax_scale, void* out, float* lse, hipStream_t st) {
   const int nqt = (int)((Sq + sage::kQueryTile - 1) / sage::kQueryTile);
   const int64_t nwg = B * H * nqt;
   if (nwg > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
   const float c = (float)softmax_scale * (float)1.4426950408889634;  // fl32(fl32(scale) * fl32(log2 e))
   const float log2_448 = (float)std::log2(448.0);
-  hipLaunchKernelGGL(sage::attn_fwd_kernel, dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st, q8, qs, k8, ks,
-                     vt, vs, (int)Sq, (int)Skv, (int)H, (int)seq_pad(Sq), (int)seq_pad(Skv), nqt, (int)nwg, c,
-                     log2_448, (uint16_t*)out, lse);
+  if (D == 64)
+    hipLaunchKernelGGL(sage::attn_fwd_kernel<64>, dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st, q8, qs, k8,
+                       ks, vt, vs, (int)Sq, (int)Skv, (int)H, (int)seq_pad(Sq), (int)seq_pad(Skv), nqt, (int)nwg, c,
+                       log2_448, (uint16_t*)out, lse);
+  else
+    hipLaunchKernelGGL(sage::attn_fwd_kernel<128>, dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st, q8, qs,
+                       k8, ks, vt, vs, (int)Sq, (int)Skv, (int)H, (int)seq_pad(Sq), (int)seq_pad(Skv), nqt, (int)nwg,
+                       c, log2_448, (uint16_t*)out, lse);
   return launched("sage_attn_fwd");
 }
 
@@ -179,18 +203,18 @@ struct WorkspaceEx {
 
 // Intermediates of sage_attention_ex, each 256-byte aligned; the scratch
 // region serves sage_quant_v and, before it, the K-smoothing block sums.
-WorkspaceEx layout_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H) {
+WorkspaceEx layout_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D) {
   WorkspaceEx w{};
   const int64_t Sqp = seq_pad(Sq), Skp = seq_pad(Skv);
   w.q8 = 0;
-  w.k8 = w.q8 + align256((size_t)(B * H * Sqp * 128));
-  w.v8 = w.k8 + align256((size_t)(B * H * Skp * 128));
-  w.qs = w.v8 + align256((size_t)(B * H * Skp * 128));
+  w.k8 = w.q8 + align256((size_t)(B * H * Sqp * D));
+  w.v8 = w.k8 + align256((size_t)(B * H * Skp * D));
+  w.qs = w.v8 + align256((size_t)(B * H * Skp * D));
   w.ks = w.qs + align256((size_t)(B * H * (Sqp / 32)) * 4);
   w.vs = w.ks + align256((size_t)(B * H * (Skp / 32)) * 4);
-  w.kmean = w.vs + align256((size_t)(B * H * 128) * 4);
-  w.scratch = w.kmean + align256((size_t)(B * H * 128) * 4);
-  const size_t a = v_scratch_bytes(B, Skv, H), b = k_smooth_scratch_bytes(B, Skv, H);
+  w.kmean = w.vs + align256((size_t)(B * H * D) * 4);
+  w.scratch = w.kmean + align256((size_t)(B * H * D) * 4);
+  const size_t a = v_scratch_bytes(B, Skv, H, D), b = k_smooth_scratch_bytes(B, Skv, H, D);
   w.scratch_bytes = a > b ? a : b;
   w.total = w.scratch + w.scratch_bytes;
   return w;
@@ -224,12 +248,12 @@ int64_t sage_seq_pad(int64_t S) { return S < 1 ? 0 : seq_pad(S); }
 
 size_t sage_quant_v_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
   if (check_shape(B, S, H, D) != SAGE_OK) return 0;
-  return v_scratch_bytes(B, S, H);
+  return v_scratch_bytes(B, S, H, D);
 }
 
 size_t sage_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
   if (check_shape(B, S, H, D) != SAGE_OK) return 0;
-  return layout(B, S, H).total;
+  return layout(B, S, H, D).total;
 }
 
 sage_status sage_quant_qk(const void* x, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* x_i8,
@@ -239,7 +263,7 @@ sage_status sage_quant_qk(const void* x, int64_t B, int64_t S, int64_t H, int64_
   SAGE_TRY(check_ptr(x_i8, "x_i8"));
   SAGE_TRY(check_ptr(x_scale, "x_scale"));
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return quant_qk_impl(x, B, S, H, x_i8, x_scale, (hipStream_t)stream);
+  return quant_qk_impl(x, B, S, H, D, x_i8, x_scale, (hipStream_t)stream);
 }
 
 sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t D, uint8_t* v_fp8_t,
@@ -249,10 +273,10 @@ sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t
   SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
   SAGE_TRY(check_ptr(v_scale, "v_scale"));
   SAGE_TRY(check_ptr(scratch, "scratch"));
-  if (scratch_bytes < v_scratch_bytes(B, S, H))
-    return fail(SAGE_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, v_scratch_bytes(B, S, H));
+  if (scratch_bytes < v_scratch_bytes(B, S, H, D))
+    return fail(SAGE_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, v_scratch_bytes(B, S, H, D));
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return quant_v_impl(v, B, S, H, v_fp8_t, v_scale, scratch, (hipStream_t)stream);
+  return quant_v_impl(v, B, S, H, D, v_fp8_t, v_scale, scratch, (hipStream_t)stream);
 }
 
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
@@ -268,7 +292,7 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
   SAGE_TRY(check_ptr(out, "out"));
   if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, S, H, softmax_scale, out, nullptr,
+  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, S, H, D, softmax_scale, out, nullptr,
                    (hipStream_t)stream);
 }
 
@@ -282,7 +306,7 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
   SAGE_TRY(check_ptr(out, "out"));
   if (!workspace) return fail(SAGE_ERR_NULL, "workspace is NULL");
   if (((uintptr_t)workspace) & 255) return fail(SAGE_ERR_ALIGN, "workspace is not 256-byte aligned");
-  const Workspace w = layout(B, S, H);
+  const Workspace w = layout(B, S, H, D);
   if (workspace_bytes < w.total)
     return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
   if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
@@ -295,16 +319,17 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
   float* qs = (float*)(ws + w.qs);
   float* ks = (float*)(ws + w.ks);
   float* vs = (float*)(ws + w.vs);
-  SAGE_TRY(quant_qk_impl(q, B, S, H, q8, qs, st));
-  SAGE_TRY(quant_qk_impl(k, B, S, H, k8, ks, st));
-  SAGE_TRY(quant_v_impl(v, B, S, H, v8, vs, ws + w.scratch, st));
-  return attn_impl(q8, qs, k8, ks, v8, vs, B, S, S, H, softmax_scale, out, nullptr, st);
+  SAGE_TRY(quant_qk_impl(q, B, S, H, D, q8, qs, st));
+  SAGE_TRY(quant_qk_impl(k, B, S, H, D, k8, ks, st));
+  SAGE_TRY(quant_v_impl(v, B, S, H, D, v8, vs, ws + w.scratch, st));
+  return attn_impl(q8, qs, k8, ks, v8, vs, B, S, S, H, D, softmax_scale, out, nullptr, st);
 }
 
 sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t B, int64_t S, int64_t H,
                                  int64_t D, int64_t b, int64_t h, int64_t r0, int64_t nr, int64_t c0,
                                  int64_t nc, int32_t* scores, void* stream) {
   SAGE_TRY(check_shape(B, S, H, D));
+  if (D != 128) return fail(SAGE_ERR_UNSUPPORTED, "the score dump covers head dim 128 only");
   SAGE_TRY(check_ptr(q_i8, "q_i8"));
   SAGE_TRY(check_ptr(k_i8, "k_i8"));
   if (!scores) return fail(SAGE_ERR_NULL, "scores is NULL");
@@ -325,7 +350,7 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
 
 size_t sage_k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
   if (check_shape(B, S, H, D) != SAGE_OK) return 0;
-  return k_smooth_scratch_bytes(B, S, H);
+  return k_smooth_scratch_bytes(B, S, H, D);
 }
 
 sage_status sage_quant_k_smooth(const void* k, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* k_i8,
@@ -337,10 +362,11 @@ sage_status sage_quant_k_smooth(const void* k, int64_t B, int64_t S, int64_t H, 
   SAGE_TRY(check_ptr(k_scale, "k_scale"));
   SAGE_TRY(check_ptr(k_mean, "k_mean"));
   SAGE_TRY(check_ptr(scratch, "scratch"));
-  if (scratch_bytes < k_smooth_scratch_bytes(B, S, H))
-    return fail(SAGE_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, k_smooth_scratch_bytes(B, S, H));
+  if (scratch_bytes < k_smooth_scratch_bytes(B, S, H, D))
+    return fail(SAGE_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes,
+                k_smooth_scratch_bytes(B, S, H, D));
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return quant_k_smooth_impl(k, B, S, H, k_i8, k_scale, k_mean, scratch, (hipStream_t)stream);
+  return quant_k_smooth_impl(k, B, S, H, D, k_i8, k_scale, k_mean, scratch, (hipStream_t)stream);
 }
 
 sage_status sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
@@ -358,13 +384,13 @@ sage_status sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int
   if (lse && (((uintptr_t)lse) & 3)) return fail(SAGE_ERR_ALIGN, "lse is not 4-byte aligned");
   if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, Sq, Skv, H, softmax_scale, out, lse,
+  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, Sq, Skv, H, D, softmax_scale, out, lse,
                    (hipStream_t)stream);
 }
 
 size_t sage_workspace_bytes_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D) {
   if (check_shape(B, Sq, H, D) != SAGE_OK || check_shape(B, Skv, H, D) != SAGE_OK) return 0;
-  return layout_ex(B, Sq, Skv, H).total;
+  return layout_ex(B, Sq, Skv, H, D).total;
 }
 
 sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64_t B, int64_t Sq, int64_t Skv,
@@ -380,7 +406,7 @@ sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64
   if (lse && (((uintptr_t)lse) & 3)) return fail(SAGE_ERR_ALIGN, "lse is not 4-byte aligned");
   if (!workspace) return fail(SAGE_ERR_NULL, "workspace is NULL");
   if (((uintptr_t)workspace) & 255) return fail(SAGE_ERR_ALIGN, "workspace is not 256-byte aligned");
-  const WorkspaceEx w = layout_ex(B, Sq, Skv, H);
+  const WorkspaceEx w = layout_ex(B, Sq, Skv, H, D);
   if (workspace_bytes < w.total)
     return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
   if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
@@ -393,13 +419,13 @@ sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64
   float* qs = (float*)(ws + w.qs);
   float* ks = (float*)(ws + w.ks);
   float* vs = (float*)(ws + w.vs);
-  SAGE_TRY(quant_qk_impl(q, B, Sq, H, q8, qs, st));
+  SAGE_TRY(quant_qk_impl(q, B, Sq, H, D, q8, qs, st));
   if (flags & SAGE_SMOOTH_K)
-    SAGE_TRY(quant_k_smooth_impl(k, B, Skv, H, k8, ks, (float*)(ws + w.kmean), ws + w.scratch, st));
+    SAGE_TRY(quant_k_smooth_impl(k, B, Skv, H, D, k8, ks, (float*)(ws + w.kmean), ws + w.scratch, st));
   else
-    SAGE_TRY(quant_qk_impl(k, B, Skv, H, k8, ks, st));
-  SAGE_TRY(quant_v_impl(v, B, Skv, H, v8, vs, ws + w.scratch, st));
-  return attn_impl(q8, qs, k8, ks, v8, vs, B, Sq, Skv, H, softmax_scale, out, lse, st);
+    SAGE_TRY(quant_qk_impl(k, B, Skv, H, D, k8, ks, st));
+  SAGE_TRY(quant_v_impl(v, B, Skv, H, D, v8, vs, ws + w.scratch, st));
+  return attn_impl(q8, qs, k8, ks, v8, vs, B, Sq, Skv, H, D, softmax_scale, out, lse, st);
 }
 
 }  // extern "C"

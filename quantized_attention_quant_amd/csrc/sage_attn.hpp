@@ -35,8 +35,17 @@
 
 namespace sage {
 
-__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_key(row)) << 4); }
+// Swizzle of LDS tiles with rows of kRB bytes (128 or 64): chunk c of row r
+// sits at chunk c ^ key(r). A 16-byte read is served for 16 lanes at a time
+// from 64 four-byte banks; 16 consecutive rows read at one logical chunk
+// then cover all 256 bytes of the banks exactly once.
+template <int kRB>
+__device__ __forceinline__ int swz_key(int row) {
+  static_assert(kRB == 128 || kRB == 64, "row sizes of the two head dims");
+  return kRB == 128 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
+template <int kRB>
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRB + ((chunk ^ swz_key<kRB>(row)) << 4); }
 
 // Cooperative copy of one 128-row x 128-byte tile (rows `row_stride` bytes
 // apart in global memory) into swizzled LDS. 256 threads, 4 x 16 B each.
@@ -47,30 +56,33 @@ __device__ __forceinline__ void stage_tile(uint8_t* __restrict__ lds, const uint
     const int idx = tid + 256 * it;
     const int row = idx >> 3, ch = idx & 7;
     const uint4 w = *(const uint4*)(src + row * row_stride + ch * 16);
-    *(uint4*)(lds + swz(row, ch)) = w;
+    *(uint4*)(lds + swz<128>(row, ch)) = w;
   }
 }
 
-// The wave's Q fragment: lane l holds bytes [64 g, 64 g + 64) of query row
-// l%32 (g = l/32); step s of the 128-deep contraction uses 16 of them. K
-// operands use the same byte mapping, so the products pair matching dims.
-__device__ __forceinline__ void load_q_frag(const int8_t* __restrict__ qrow, v4i qf[4]) {
+// The wave's Q fragment for head dim kD: lane l holds bytes
+// [kD/2 g, kD/2 g + kD/2) of query row l%32 (g = l/32, qrow points there);
+// step s of the kD-deep contraction uses 16 of them. K operands use the same
+// byte mapping, so the products pair matching dims.
+template <int kD>
+__device__ __forceinline__ void load_q_frag(const int8_t* __restrict__ qrow, v4i qf[kD / 32]) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qf[s] = *(const v4i*)(qrow + 16 * s);
+  for (int s = 0; s < kD / 32; ++s) qf[s] = *(const v4i*)(qrow + 16 * s);
 }
 
 // S^T for the 128 keys of the staged tile against the wave's 32 queries:
 // sacc[u] covers keys [32 u, 32 u + 32) of the tile; every accumulator
 // starts from `init`.
-__device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ lds_k, const v4i qf[4], int li, int g,
+template <int kD>
+__device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ lds_k, const v4i qf[kD / 32], int li, int g,
                                         const v16i& init, v16i sacc[4]) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     v16i acc = init;
     const int row = 32 * u + li;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const v4i kop = *(const v4i*)(lds_k + swz(row, 4 * g + s));
+    for (int s = 0; s < kD / 32; ++s) {
+      const v4i kop = *(const v4i*)(lds_k + swz<kD>(row, (kD / 32) * g + s));
       acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop, qf[s], acc, 0, 0, 0);
     }
     sacc[u] = acc;
@@ -182,9 +194,9 @@ struct RowState {
 
 // Vector phase of one key tile for one wave: running max, rescale of l and
 // O, P' and its FP8 codes.
-template <bool kTail>
+template <int kD, bool kTail>
 __device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const float* __restrict__ ks4, float c,
-                                             float log2_448, int nvalid, int g, RowState& st, v16f o[4],
+                                             float log2_448, int nvalid, int g, RowState& st, v16f o[kD / 32],
                                              v8i pop[2]) {
   float f[4];
 #pragma unroll
@@ -230,21 +242,22 @@ __device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const fl
   st.l = st.l * alpha + lsum;
   if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) o[cb] *= alpha;
+    for (int cb = 0; cb < kD / 32; ++cb) o[cb] *= alpha;
   }
   st.m = m_new;
   st.m2 = m2_new;
 }
 
 // O^T += V^T . P^T for one 128-key tile (8 FP8 MFMAs).
-__device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int li, int g, v16f o[4]) {
+template <int kD>
+__device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int li, int g, v16f o[kD / 32]) {
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kD / 32; ++cb) {
       const int row = 32 * cb + li;
-      const v4i lo = *(const v4i*)(lv + swz(row, 4 * w + 2 * g));
-      const v4i hi = *(const v4i*)(lv + swz(row, 4 * w + 2 * g + 1));
+      const v4i lo = *(const v4i*)(lv + swz<128>(row, 4 * w + 2 * g));
+      const v4i hi = *(const v4i*)(lv + swz<128>(row, 4 * w + 2 * g + 1));
       const v8i vop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop[w], o[cb], 0, 0, 0, 0, 0, 0);
     }
@@ -265,6 +278,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int
 // wave's vector work fills the cycles between them. Interval i reads K tiles i, i+1 and V tiles i-1, i,
 // and loads K tile i+2 and V tile i+1 into the third slot of each
 // three-stage LDS ring.
+template <int kD>
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qscale,
                      const int8_t* __restrict__ k8, const float* __restrict__ kscale,
@@ -272,8 +286,10 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
                      int H, int Sq_pad, int Skv_pad, int nqt, int num_wg, float c, float log2_448,
                      uint16_t* __restrict__ out, float* __restrict__ lse) {
   static_assert(kAttnWaves == 8, "the phase skew pairs waves w and w + 4");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[3][kKeyTile * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[3][kKeyTile * 128];
+  static_assert(kD == 128 || kD == 64, "head dims 64 and 128");
+  // K tile: kKeyTile rows of kD bytes; V^T tile: kD rows of kKeyTile bytes
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[3][kKeyTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[3][kD * kKeyTile];
 
   const int wg = xcd_remap(blockIdx.x, num_wg);
   const int qt = wg % nqt;
@@ -284,61 +300,67 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   const bool lead = wave_s < 4;
   const int q0 = qt * kQueryTile + wave * 32;
 
-  const uint8_t* kbase = (const uint8_t*)k8 + bh * Skv_pad * kHeadDim;
-  const uint8_t* vbase = v8t + bh * kHeadDim * (int64_t)Skv_pad;
+  const uint8_t* kbase = (const uint8_t*)k8 + bh * Skv_pad * kD;
+  const uint8_t* vbase = v8t + bh * kD * (int64_t)Skv_pad;
   const float* ksb = kscale + bh * (Skv_pad / kQBlock);
   const int T = (Skv + kKeyTile - 1) / kKeyTile;
 
   // Tiles stream into LDS with buffer_load ... lds: lane l of a wave
-  // instruction writes LDS bytes [16 l, 16 l + 16) of an 8-row group, i.e.
-  // row 8 grp + l/8 and swizzled chunk l%8, so it reads source chunk
-  // (l%8) ^ key(row). The lane offsets are loop-invariant; the tile offset is
-  // a scalar. Buffer descriptors cover this head's K rows and V^T rows
-  // (base, stride 0, size in bytes < 2^31, default data format).
+  // instruction writes LDS bytes [16 l, 16 l + 16) of a 1 KB group of rows
+  // (K: 1024/kD rows of kD bytes; V^T: 8 rows of 128 bytes), i.e. row
+  // grp * rows_per_group + l / chunks_per_row and swizzled chunk
+  // l % chunks_per_row, so it reads the source chunk XORed with the row's
+  // swizzle key. A tile is kD/8 groups, kD/64 per wave. The lane offsets are
+  // loop-invariant; the tile offset is a scalar. Buffer descriptors cover
+  // this head's K rows and V^T rows (base, stride 0, size in bytes < 2^31,
+  // default data format).
   const uint64_t kaddr = (uint64_t)(uintptr_t)kbase, vaddr = (uint64_t)(uintptr_t)vbase;
-  const uint32_t nbytes = (uint32_t)Skv_pad * kHeadDim;
+  const uint32_t nbytes = (uint32_t)Skv_pad * kD;
   const v4i rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)kaddr),
                   __builtin_amdgcn_readfirstlane((int)(uint32_t)(kaddr >> 32) & 0xFFFF),
                   __builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000};
   const v4i rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)vaddr),
                   __builtin_amdgcn_readfirstlane((int)(uint32_t)(vaddr >> 32) & 0xFFFF),
                   __builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000};
-  uint32_t koff[2], voff[2];
+  constexpr int kGroupsPerWave = kD / 64;
+  constexpr int kKChunks = kD / 16;   // 16-byte chunks per K row
+  uint32_t koff[kGroupsPerWave], voff[kGroupsPerWave];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 8 * (wave + 8 * i) + (lane >> 3);
-    const int chunk = ((lane & 7) ^ swz_key(row)) << 4;
-    koff[i] = (uint32_t)(row * kHeadDim + chunk);
-    voff[i] = (uint32_t)(row * Skv_pad + chunk);
+  for (int i = 0; i < kGroupsPerWave; ++i) {
+    const int grp = wave + 8 * i;
+    const int krow = (1024 / kD) * grp + lane / kKChunks;
+    koff[i] = (uint32_t)(krow * kD + (((lane % kKChunks) ^ swz_key<kD>(krow)) << 4));
+    const int vrow = 8 * grp + (lane >> 3);
+    voff[i] = (uint32_t)(vrow * Skv_pad + (((lane & 7) ^ swz_key<128>(vrow)) << 4));
   }
   // LDS byte address of the first 1 KB row group this wave writes per slot.
   const uint32_t kl0 = lds_addr(lds_k[0]) + wave_s * 1024, vl0 = lds_addr(lds_v[0]) + wave_s * 1024;
   auto load_k = [&](int t, int slot) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16(rk, kl0 + slot * (kKeyTile * 128) + i * 8192, koff[i], (uint32_t)t * (kKeyTile * kHeadDim));
+    for (int i = 0; i < kGroupsPerWave; ++i)
+      dma16(rk, kl0 + slot * (kKeyTile * kD) + i * 8192, koff[i], (uint32_t)t * (kKeyTile * kD));
   };
   auto load_v = [&](int t, int slot) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16(rv, vl0 + slot * (kKeyTile * 128) + i * 8192, voff[i], (uint32_t)t * kKeyTile);
+    for (int i = 0; i < kGroupsPerWave; ++i)
+      dma16(rv, vl0 + slot * (kD * kKeyTile) + i * 8192, voff[i], (uint32_t)t * kKeyTile);
   };
 
   load_k(0, 0);
   load_v(0, 0);
   if (T > 1) load_k(1, 1);
 
-  v4i qf[4];
-  load_q_frag(q8 + ((bh * Sq_pad + q0 + li) * kHeadDim + 64 * g), qf);
+  v4i qf[kD / 32];
+  load_q_frag<kD>(q8 + ((bh * Sq_pad + q0 + li) * kD + (kD / 2) * g), qf);
   const float qs = qscale[bh * (Sq_pad / kQBlock) + q0 / kQBlock];
 
   v16i bias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) bias[r] = kScoreBias;
   RowState st{-INFINITY, -INFINITY, 0.0f};
-  v16f o[4];
+  v16f o[kD / 32];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) o[cb] = (v16f){0};
+  for (int cb = 0; cb < kD / 32; ++cb) o[cb] = (v16f){0};
   v16i s[4];
   v8i pop[2];
 
@@ -350,41 +372,41 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   // i % 3 of both rings. The last interval (i = T-1), whose tile may be
   // ragged (keys >= Skv masked), has no barrier after it.
   if (lead) {
-    qk_tile(lds_k[0], qf, li, g, bias, s);
+    qk_tile<kD>(lds_k[0], qf, li, g, bias, s);
     for (int i = 0; i < T - 1; ++i) {
       const int sl = i % 3;
       if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
       load_v(i + 1, (sl + 1) % 3);
-      vector_phase<false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
+      vector_phase<kD, false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
       __builtin_amdgcn_s_setprio(2);
-      pv_tile(lds_v[sl], pop, li, g, o);
-      qk_tile(lds_k[(sl + 1) % 3], qf, li, g, bias, s);
+      pv_tile<kD>(lds_v[sl], pop, li, g, o);
+      qk_tile<kD>(lds_k[(sl + 1) % 3], qf, li, g, bias, s);
       __builtin_amdgcn_s_setprio(0);
       wait_tiles();
       __syncthreads();
     }
     const int i = T - 1;
-    vector_phase<true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
-    pv_tile(lds_v[i % 3], pop, li, g, o);
+    vector_phase<kD, true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
+    pv_tile<kD>(lds_v[i % 3], pop, li, g, o);
   } else {
     for (int i = 0; i < T - 1; ++i) {
       const int sl = i % 3;
       if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
       load_v(i + 1, (sl + 1) % 3);
       __builtin_amdgcn_s_setprio(2);
-      if (i > 0) pv_tile(lds_v[(sl + 2) % 3], pop, li, g, o);
-      qk_tile(lds_k[sl], qf, li, g, bias, s);
+      if (i > 0) pv_tile<kD>(lds_v[(sl + 2) % 3], pop, li, g, o);
+      qk_tile<kD>(lds_k[sl], qf, li, g, bias, s);
       __builtin_amdgcn_s_setprio(0);
-      vector_phase<false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
+      vector_phase<kD, false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
       wait_tiles();
       __syncthreads();
     }
     const int i = T - 1;
     const int sl = i % 3;
-    if (i > 0) pv_tile(lds_v[(sl + 2) % 3], pop, li, g, o);
-    qk_tile(lds_k[sl], qf, li, g, bias, s);
-    vector_phase<true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
-    pv_tile(lds_v[sl], pop, li, g, o);
+    if (i > 0) pv_tile<kD>(lds_v[(sl + 2) % 3], pop, li, g, o);
+    qk_tile<kD>(lds_k[sl], qf, li, g, bias, s);
+    vector_phase<kD, true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
+    pv_tile<kD>(lds_v[sl], pop, li, g, o);
   }
 
   // Epilogue: O = acc * v_scale / l, bf16, layout [B, Sq, H, D]; optional
@@ -400,10 +422,10 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   if (qi < Sq) {
     const int h = (int)(bh % H);
     const int64_t b = bh / H;
-    uint16_t* orow = out + ((b * Sq + qi) * H + h) * kHeadDim;
-    const float* vsb = vscale + bh * kHeadDim;
+    uint16_t* orow = out + ((b * Sq + qi) * H + h) * kD;
+    const float* vsb = vscale + bh * kD;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kD / 32; ++cb) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int c0 = 32 * cb + 8 * rg + 4 * g;
@@ -431,10 +453,10 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict_
   __syncthreads();
   if (qa >= S_pad) return;
   v4i qf[4];
-  load_q_frag(q8 + ((bh * S_pad + qa + li) * kHeadDim + 64 * g), qf);
+  load_q_frag<kHeadDim>(q8 + ((bh * S_pad + qa + li) * kHeadDim + 64 * g), qf);
   v16i sacc[4];
   const v16i zero = {0};
-  qk_tile(lds_k, qf, li, g, zero, sacc);
+  qk_tile<kHeadDim>(lds_k, qf, li, g, zero, sacc);
   const int row = qa + li;
   if (row < r0 || row >= r0 + nr) return;
 #pragma unroll

@@ -11,11 +11,12 @@
 
 namespace sage {
 
-// One wave per (b, h, 32-row block); 4 waves per workgroup.
-// Lane l covers columns [8 (l%16), +8) of rows 4 it + l/16, it = 0..7.
+// One wave per (b, h, 32-row block); 4 waves per workgroup; head dim kD.
+// With L = kD/8 lanes per row, lane l covers columns [8 (l%L), +8) of rows
+// (64/L) it + l/L, it = 0 .. 32 L/64 - 1.
 // kSmooth: the values quantized are fl32(x - xmean[b, h, c]) (K smoothing);
 // rows >= S stay zero.
-template <bool kSmooth>
+template <int kD, bool kSmooth>
 __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restrict__ x, int S, int H,
                                                        int S_pad, int nbp, int64_t total_blocks,
                                                        const float* __restrict__ xmean,
@@ -28,21 +29,22 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
   const int64_t bh = blk / nbp;
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
-  const int col = (lane & 15) * 8;
+  constexpr int kLanesPerRow = kD / 8, kRowsPerIt = 64 / kLanesPerRow, kIters = kQBlock / kRowsPerIt;
+  const int col = (lane % kLanesPerRow) * 8;
   const int r0 = t * kQBlock;
 
   float mu[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (kSmooth) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mu[j] = xmean[bh * kHeadDim + col + j];
+    for (int j = 0; j < 8; ++j) mu[j] = xmean[bh * kD + col + j];
   }
-  float v[8][8];
+  float v[kIters][8];
   float amax = 0.0f;
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int row = r0 + it * 4 + (lane >> 4);
+  for (int it = 0; it < kIters; ++it) {
+    const int row = r0 + it * kRowsPerIt + lane / kLanesPerRow;
     uint4 w = make_uint4(0, 0, 0, 0);
-    if (row < S) w = *(const uint4*)(x + (((b * S + row) * H + h) * kHeadDim + col));
+    if (row < S) w = *(const uint4*)(x + (((b * S + row) * H + h) * kD + col));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -64,8 +66,8 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
     if (!isfinite(inv)) { inv = 0.0f; scale = 0.0f; }
   }
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int row = r0 + it * 4 + (lane >> 4);
+  for (int it = 0; it < kIters; ++it) {
+    const int row = r0 + it * kRowsPerIt + lane / kLanesPerRow;
     uint32_t packed[2] = {0, 0};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -74,28 +76,30 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
       const uint32_t byte = (uint32_t)((int)y) & 0xFFu;
       packed[j >> 2] |= byte << (8 * (j & 3));
     }
-    *(uint2*)(xq + ((bh * S_pad + row) * kHeadDim + col)) = make_uint2(packed[0], packed[1]);
+    *(uint2*)(xq + ((bh * S_pad + row) * kD + col)) = make_uint2(packed[0], packed[1]);
   }
   if (lane == 0) xscale[bh * nbp + t] = scale;
 }
 
 // Partial per-channel amax of |V| over a chunk of kVChunkRows rows.
-// grid (nchunk, B*H), 256 threads: thread t covers channels [8 (t%16), +8)
-// of rows t/16 + 16 i.
+// grid (nchunk, B*H), 256 threads: with G = kD/8 channel groups, thread t
+// covers channels [8 (t%G), +8) of rows t/G + (256/G) i.
+template <int kD>
 __global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __restrict__ v, int S,
                                                              int H, int nchunk,
                                                              float* __restrict__ partial) {
-  __shared__ float red[16][kHeadDim];
+  constexpr int kGroups = kD / 8, kRowSets = 256 / kGroups;
+  __shared__ float red[kRowSets][kD];
   const int chunk = blockIdx.x;
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
-  const int cg = threadIdx.x & 15, ro = threadIdx.x >> 4;
+  const int cg = threadIdx.x % kGroups, ro = threadIdx.x / kGroups;
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int rbeg = chunk * kVChunkRows;
   const int rend = min(S, rbeg + kVChunkRows);
-  for (int row = rbeg + ro; row < rend; row += 16) {
-    const uint4 w = *(const uint4*)(v + (((b * S + row) * H + h) * kHeadDim + cg * 8));
+  for (int row = rbeg + ro; row < rend; row += kRowSets) {
+    const uint4 w = *(const uint4*)(v + (((b * S + row) * H + h) * kD + cg * 8));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -106,45 +110,47 @@ __global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __r
 #pragma unroll
   for (int j = 0; j < 8; ++j) red[ro][cg * 8 + j] = m[j];
   __syncthreads();
-  if (threadIdx.x < kHeadDim) {
+  if (threadIdx.x < kD) {
     float r = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) r = fmaxf(r, red[i][threadIdx.x]);
-    partial[(bh * nchunk + chunk) * kHeadDim + threadIdx.x] = r;
+    for (int i = 0; i < kRowSets; ++i) r = fmaxf(r, red[i][threadIdx.x]);
+    partial[(bh * nchunk + chunk) * kD + threadIdx.x] = r;
   }
 }
 
 // Per-channel amax over all chunks -> v_scale and the fp32 reciprocal.
-// grid B*H, 128 threads (one per channel).
+// grid B*H, kD threads (one per channel).
+template <int kD>
 __global__ __launch_bounds__(128) void v_scale_kernel(const float* __restrict__ partial, int nchunk,
                                                       float* __restrict__ vscale,
                                                       float* __restrict__ vinv) {
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
   float amax = 0.0f;
-  for (int i = 0; i < nchunk; ++i) amax = fmaxf(amax, partial[(bh * nchunk + i) * kHeadDim + c]);
+  for (int i = 0; i < nchunk; ++i) amax = fmaxf(amax, partial[(bh * nchunk + i) * kD + c]);
   float scale = 0.0f, inv = 0.0f;
   if (amax > 0.0f) {
     inv = __fdiv_rn(448.0f, amax);
     scale = __fdiv_rn(amax, 448.0f);
     if (!isfinite(inv)) { inv = 0.0f; scale = 0.0f; }
   }
-  vscale[bh * kHeadDim + c] = scale;
-  vinv[bh * kHeadDim + c] = inv;
+  vscale[bh * kD + c] = scale;
+  vinv[bh * kD + c] = inv;
 }
 
 // Quantize 128 keys x 128 channels of V to E4M3FN and write them transposed
 // ([channel][key]) with keys permuted inside each 64-key group.
-// grid (S_pad/128, B*H), 256 threads. Thread t covers channels
+// grid (S_pad/128, B*H), 2 kD threads. Thread t covers channels
 // [8 (t/16), +8) of 8 keys that land in 8 consecutive slots: within a 32-key
 // block u of a 64-key group, key 32u + 4m + e (m = 0..7, e = 0..3) goes to
 // slot 32 (m%2) + 16u + 4 (m/2) + e, so quads m = g + 4pr and g + 4pr + 2
 // fill slots [32g + 16u + 8pr, +8). The 16 threads of a channel group write
 // one 128-byte row of the LDS tile between them.
+template <int kD>
 __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict__ v, int S, int H,
                                                       int S_pad, const float* __restrict__ vinv,
                                                       uint8_t* __restrict__ vt) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim][128 + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kD][128 + 16];
   const int k0 = blockIdx.x * 128;
   const int64_t bh = blockIdx.y;
   const int h = (int)(bh % H);
@@ -155,13 +161,13 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
   const int slot = 64 * grp + 32 * g + 16 * u + 8 * pr;
   float inv[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) inv[j] = vinv[bh * kHeadDim + cg * 8 + j];
+  for (int j = 0; j < 8; ++j) inv[j] = vinv[bh * kD + cg * 8 + j];
   float y[8][8];   // [key][channel]
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int row = k0 + kq0 + (e & 3) + 8 * (e >> 2);
     uint4 w = make_uint4(0, 0, 0, 0);
-    if (row < S) w = *(const uint4*)(v + (((b * S + row) * H + h) * kHeadDim + cg * 8));
+    if (row < S) w = *(const uint4*)(v + (((b * S + row) * H + h) * kD + cg * 8));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
   }
   __syncthreads();
   const int c = threadIdx.x >> 1, half = threadIdx.x & 1;
-  uint8_t* dst = vt + (bh * kHeadDim + c) * (int64_t)S_pad + k0 + 64 * half;
+  uint8_t* dst = vt + (bh * kD + c) * (int64_t)S_pad + k0 + 64 * half;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     *(uint4*)(dst + 16 * q) = *(const uint4*)(&tile[c][64 * half + 16 * q]);
@@ -187,23 +193,25 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
 
 // K smoothing, step 1: per (b, h, 32-row block) fp32 sum of each channel,
 // rows added one at a time in increasing s (rows >= S contribute nothing).
-// Four blocks per wave: lane l covers channels [8 (l%16), +8) of block
-// 4 (4 blockIdx + wave) + l/16.
+// With L = kD/8 lanes per block, 64/L blocks per wave: lane l covers
+// channels [8 (l%L), +8) of block (64/L) (4 blockIdx + wave) + l/L.
+template <int kD>
 __global__ __launch_bounds__(256) void k_block_sum_kernel(const uint16_t* __restrict__ k, int S, int H,
                                                           int nbp, int64_t total_blocks,
                                                           float* __restrict__ partial) {
+  constexpr int kLanesPerBlock = kD / 8, kBlocksPerWave = 64 / kLanesPerBlock;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t blk = ((int64_t)blockIdx.x * 4 + wave) * 4 + (lane >> 4);
+  const int64_t blk = ((int64_t)blockIdx.x * 4 + wave) * kBlocksPerWave + lane / kLanesPerBlock;
   if (blk >= total_blocks) return;
   const int t = (int)(blk % nbp);
   const int64_t bh = blk / nbp;
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
-  const int col = (lane & 15) * 8;
+  const int col = (lane % kLanesPerBlock) * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int rend = min(S, (t + 1) * kQBlock);
   for (int row = t * kQBlock; row < rend; ++row) {
-    const uint4 w = *(const uint4*)(k + (((b * S + row) * H + h) * kHeadDim + col));
+    const uint4 w = *(const uint4*)(k + (((b * S + row) * H + h) * kD + col));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -211,21 +219,22 @@ __global__ __launch_bounds__(256) void k_block_sum_kernel(const uint16_t* __rest
       acc[2 * j + 1] = acc[2 * j + 1] + bf16_to_f32(ws[j] >> 16);
     }
   }
-  float4* dst = (float4*)(partial + blk * kHeadDim + col);
+  float4* dst = (float4*)(partial + blk * kD + col);
   dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 // K smoothing, step 2: the block sums added in block order, then
-// mean = fl32(sum / S). grid B*H, 128 threads (one per channel).
+// mean = fl32(sum / S). grid B*H, kD threads (one per channel).
+template <int kD>
 __global__ __launch_bounds__(128) void k_mean_kernel(const float* __restrict__ partial, int nbp, int S,
                                                      float* __restrict__ kmean) {
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
-  const float* p = partial + bh * (int64_t)nbp * kHeadDim + c;
+  const float* p = partial + bh * (int64_t)nbp * kD + c;
   float sum = 0.0f;
-  for (int t = 0; t < nbp; ++t) sum = sum + p[(int64_t)t * kHeadDim];
-  kmean[bh * kHeadDim + c] = __fdiv_rn(sum, (float)S);
+  for (int t = 0; t < nbp; ++t) sum = sum + p[(int64_t)t * kD];
+  kmean[bh * kD + c] = __fdiv_rn(sum, (float)S);
 }
 
 }  // namespace sage

@@ -58,7 +58,10 @@ def test_queries():
         ws = sage.sage_workspace_bytes(B, S, H, 128)
         base = 3 * B * H * Sp * 128
         assert base <= ws <= base * 1.02 + 65536
-    assert sage.sage_workspace_bytes(1, 256, 2, 64) == 0
+    assert sage.sage_workspace_bytes(1, 256, 2, 96) == 0
+    # head dim 64: half the bytes of the one-byte tensors
+    assert sage.sage_workspace_bytes(1, 256, 2, 64) < sage.sage_workspace_bytes(1, 256, 2, 128)
+    assert sage.sage_workspace_bytes(1, 256, 2, 64) >= 3 * 2 * 256 * 64
     assert sage.sage_workspace_bytes(0, 256, 2, 128) == 0
     assert sage.lib().sage_status_str(ERR_WS) == b"SAGE_ERR_WORKSPACE"
 
@@ -73,8 +76,11 @@ def test_validation_codes():
     f, m = p(FAKE), p(MISALIGNED)
     z = p(0)
     # head dim, sizes
-    assert _call("sage_quant_qk", f, 1, 256, 2, 64, f, f, z) == ERR_UNSUP
+    assert _call("sage_quant_qk", f, 1, 256, 2, 96, f, f, z) == ERR_UNSUP
+    assert _call("sage_quant_qk", f, 1, 256, 2, 256, f, f, z) == ERR_UNSUP
     assert _call("sage_quant_qk", f, 0, 256, 2, 128, f, f, z) == ERR_SHAPE
+    # the score dump covers head dim 128 only
+    assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 64, 0, 0, 0, 1, 0, 1, f, z) == ERR_UNSUP
     assert _call("sage_quant_qk", f, 1, -5, 2, 128, f, f, z) == ERR_SHAPE
     assert _call("sage_quant_qk", f, 1, 1 << 40, 2, 128, f, f, z) == ERR_SHAPE
     assert _call("sage_quant_qk", f, 1, (1 << 24) + 1, 2, 128, f, f, z) == ERR_SHAPE
@@ -109,7 +115,8 @@ def test_extended_entry_points_validation():
         if Sq == Skv:
             assert ws >= sage.sage_workspace_bytes(B, Sq, H, 128)
     assert sage.sage_workspace_bytes_ex(1, 300, 0, 2, 128) == 0
-    assert sage.sage_workspace_bytes_ex(1, 300, 77, 2, 64) == 0
+    assert sage.sage_workspace_bytes_ex(1, 300, 77, 2, 96) == 0
+    assert 0 < sage.sage_workspace_bytes_ex(1, 300, 77, 2, 64) < sage.sage_workspace_bytes_ex(1, 300, 77, 2, 128)
     nb = sage.sage_k_smooth_scratch_bytes(1, 300, 2, 128)
     assert nb >= 2 * (sage.sage_seq_pad(300) // 32) * 128 * 4
     # sage_quant_k_smooth
@@ -117,6 +124,7 @@ def test_extended_entry_points_validation():
     assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, f, f, z, f, nb, z) == ERR_NULL
     assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, m, f, f, f, nb, z) == ERR_ALIGN
     assert _call("sage_quant_k_smooth", f, 1, 300, 2, 96, f, f, f, f, nb, z) == ERR_UNSUP
+    assert sage.sage_k_smooth_scratch_bytes(1, 300, 2, 64) * 2 == sage.sage_k_smooth_scratch_bytes(1, 300, 2, 128)
     # sage_attn_fwd_ex: both lengths are checked, lse alignment is checked
     args = [f, f, f, f, f, f]
     assert _call("sage_attn_fwd_ex", *args, 1, 300, 0, 2, 128, fl, f, z, z) == ERR_SHAPE
@@ -146,7 +154,8 @@ def test_forced_launch_failure_hook(monkeypatch):
     assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, f, f, f, f, nb, z) == ERR_HIP
     assert _call("sage_attn_fwd_ex", f, f, f, f, f, f, 1, 300, 77, 2, 128, ctypes.c_float(0.1), f, f, z) == ERR_HIP
     # validation still runs first
-    assert _call("sage_quant_qk", f, 1, 256, 2, 64, f, f, z) == ERR_UNSUP
+    assert _call("sage_quant_qk", f, 1, 256, 2, 96, f, f, z) == ERR_UNSUP
+    assert _call("sage_quant_qk", f, 1, 256, 2, 64, f, f, z) == ERR_HIP
 
 
 def test_binding_raises_on_missing_library(monkeypatch):

@@ -187,3 +187,31 @@ def test_equal_lengths_reproduce_self_attention_rows():
     rows = np.array([0, 31, 32, 150, 199])
     part = sage_attention(q, k, v, SCALE, 128, rows=rows)
     assert np.array_equal(full[:, rows], part[:, rows])
+
+
+# ------------------------------------------------------------ head dim 64
+
+def _d64(x):
+    return np.ascontiguousarray(x[..., :64])
+
+
+@pytest.mark.parametrize("idx,Sq,Skv", [(1, 256, 256), (2, 300, 77), (5, 129, 500)])
+def test_head_dim_64_close_to_exact(idx, Sq, Skv):
+    q, k, v = _cross_inputs(idx, Sq, Skv)
+    q, k, v = _d64(q), _d64(k), _d64(v)
+    scale = 1.0 / math.sqrt(64)
+    o, lse = sage_attention(q, k, v, scale, 128, return_lse=True)
+    e, lse_exact = exact_attention_fp64(q, k, v, scale, return_lse=True)
+    assert o.shape == q.shape
+    assert _cos(o, e) >= 0.99
+    assert np.max(np.abs(lse - lse_exact)) < 0.05
+
+
+def test_head_dim_64_quantization_matches_per_channel_slices():
+    # channels are independent in V's quantization and K's mean: the first
+    # 64 channels of a D=128 call equal a D=64 call on those channels
+    _, k, v = workloads.generate(3, S=300, H=2, B=1, seed=77)
+    v8, vs = quant_v(v)
+    v8h, vsh = quant_v(_d64(v))
+    assert np.array_equal(v8[..., :64], v8h) and np.array_equal(vs[..., :64], vsh)
+    assert np.array_equal(k_mean(k)[..., :64], k_mean(_d64(k)))
