@@ -33,6 +33,9 @@
  *     fall back for it: the VAE's head dim 64, diffusers PR #15060, section
  *     "What does this PR do?"); every "128" channel count below then reads
  *     D. Other head dims return SAGE_ERR_UNSUPPORTED.
+ *   - softmax_scale must be finite and >= 0 (SAGE_ERR_SHAPE otherwise): the
+ *     kernels take each key block's maximum on the integer scores, which
+ *     orders the scaled scores only for a non-negative factor.
  *   - Inputs containing NaN/Inf, or whose scaled scores overflow fp32, are
  *     outside the contract (no guarantee on the output).
  */

@@ -290,7 +290,8 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
   SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
   SAGE_TRY(check_ptr(v_scale, "v_scale"));
   SAGE_TRY(check_ptr(out, "out"));
-  if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
+  if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
+    return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite and >= 0");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
   return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, S, H, D, softmax_scale, out, nullptr,
                    (hipStream_t)stream);
@@ -309,7 +310,8 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
   const Workspace w = layout(B, S, H, D);
   if (workspace_bytes < w.total)
     return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
-  if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
+  if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
+    return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite and >= 0");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
@@ -382,7 +384,8 @@ sage_status sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int
   SAGE_TRY(check_ptr(v_scale, "v_scale"));
   SAGE_TRY(check_ptr(out, "out"));
   if (lse && (((uintptr_t)lse) & 3)) return fail(SAGE_ERR_ALIGN, "lse is not 4-byte aligned");
-  if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
+  if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
+    return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite and >= 0");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
   return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, Sq, Skv, H, D, softmax_scale, out, lse,
                    (hipStream_t)stream);
@@ -409,7 +412,8 @@ sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64
   const WorkspaceEx w = layout_ex(B, Sq, Skv, H, D);
   if (workspace_bytes < w.total)
     return fail(SAGE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
-  if (!std::isfinite(softmax_scale)) return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite");
+  if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
+    return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite and >= 0");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;

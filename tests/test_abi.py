@@ -95,6 +95,8 @@ def test_validation_codes():
     assert _call("sage_attention", f, f, f, 1, 256, 2, 128, ctypes.c_float(0.1), f, f, ws - 1, z) == ERR_WS
     assert _call("sage_attention", f, f, f, 1, 256, 2, 128, ctypes.c_float(0.1), f, p(FAKE + 16), ws, z) == ERR_ALIGN
     assert _call("sage_attention", f, f, f, 1, 256, 2, 128, ctypes.c_float(float("nan")), f, f, ws, z) == ERR_SHAPE
+    assert _call("sage_attention", f, f, f, 1, 256, 2, 128, ctypes.c_float(-0.1), f, f, ws, z) == ERR_SHAPE
+    assert _call("sage_attn_fwd", f, f, f, f, f, f, 1, 256, 2, 128, ctypes.c_float(-1.0), f, z) == ERR_SHAPE
     assert _call("sage_attn_fwd", f, f, f, f, f, z, 1, 256, 2, 128, ctypes.c_float(0.1), f, z) == ERR_NULL
     # debug window
     assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 128, 0, 0, 0, 256, 0, 257, f, z) == ERR_RANGE
