@@ -3,6 +3,8 @@
 // Source: diffusers issue #15014, "gfx1201 (RDNA4) SageAttention attention
 // backend: aiter package or Hub kernel?", problem statement: INT8 QK^T and
 // FP8 PV with FP32 accumulation, bf16 [B, S, H, 128], no mask, non-causal.
+// Also instantiated for head dim 64, and for query and key sequences of
+// different lengths, with an optional per-row log-sum-exp.
 // The online (flash-style) softmax streams key tiles; P is quantized to FP8
 // E4M3FN with the fixed scale 448 (the largest E4M3FN value), folded into the
 // exponent of exp2.
@@ -25,10 +27,10 @@
 //        (A = V^T rows from LDS, B = P straight from registers). The V^T
 //        layout stores keys in the order the score accumulator leaves them,
 //        so no shuffles are needed between the two products.
-// LDS tiles are rows of 128 bytes whose 16-byte chunks are XOR-swizzled by
-// (row / 2) % 8: a 16-byte read is served for 16 lanes at a time from 64
-// four-byte banks, and the 16 rows a lane group reads then cover all 256
-// bytes of the banks exactly once.
+// LDS tiles are rows of 128 bytes (64 for K at head dim 64) whose 16-byte
+// chunks are XOR-swizzled (swz_key): a 16-byte read is served for 16 lanes
+// at a time from 64 four-byte banks, and the 16 rows a lane group reads then
+// cover all 256 bytes of the banks exactly once.
 #pragma once
 
 #include "sage_common.hpp"

@@ -6,14 +6,11 @@
 
 namespace sage {
 
-constexpr int kHeadDim = 128;     // the only head size of the method
+constexpr int kHeadDim = 128;     // the pages' head size (64 is also supported)
 constexpr int kQBlock = 32;       // Q/K quantization block (rows)
 constexpr int kSeqAlign = 256;    // padding of the quantized layouts
 constexpr int kKeyTile = 128;     // BN: keys per online-softmax tile
-#ifndef SAGE_ATTN_WAVES
-#define SAGE_ATTN_WAVES 8
-#endif
-constexpr int kAttnWaves = SAGE_ATTN_WAVES;     // waves per attention workgroup
+constexpr int kAttnWaves = 8;     // waves per attention workgroup
 constexpr int kQueryTile = 32 * kAttnWaves;     // BM: queries per workgroup
 constexpr int kDebugRows = 128;                 // query rows per debug-dump workgroup
 constexpr int kVGroup = 64;       // keys per permuted group of the V^T layout
