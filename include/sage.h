@@ -146,9 +146,10 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
                           void* stream);
 
 /*
- * sage_attention - one call: sage_quant_qk(Q), sage_quant_qk(K),
- * sage_quant_v(V) and sage_attn_fwd, with every intermediate inside the
- * caller's workspace (>= sage_workspace_bytes(B, S, H, D) bytes, 256-byte
+ * sage_attention - one call: sage_quant_qk(K), sage_quant_v(V) and the
+ * attention with Q quantized inside the kernel (sage_attn_fwd_qbf16; the
+ * result equals sage_quant_qk(Q) followed by sage_attn_fwd), with every
+ * intermediate inside the caller's workspace (>= sage_workspace_bytes(B, S, H, D) bytes, 256-byte
  * aligned). This is the gfx1201_sage_attention(q, k, v, softmax_scale)
  * operation of the issue's problem statement. q, k, v, out: bf16
  * [B, S, H, D].
@@ -238,6 +239,20 @@ size_t sage_workspace_bytes_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H, in
 sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64_t B, int64_t Sq, int64_t Skv,
                               int64_t H, int64_t D, float softmax_scale, unsigned flags, void* out, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sage_attn_fwd_qbf16 - sage_attn_fwd_ex with Q given as bf16 [B, Sq, H, D]
+ * and quantized inside the attention kernel, as the pages' kernel quantizes
+ * its inputs "inside the kernel" (diffusers issue #15014, problem
+ * statement). Each wave's 32 query rows are exactly one quantization block,
+ * so the codes and scales equal sage_quant_qk's bit for bit and the output
+ * equals sage_attn_fwd_ex on sage_quant_qk(Q). K and V come quantized
+ * (reusable across calls that share them). sage_attention and
+ * sage_attention_ex use this path.
+ */
+sage_status sage_attn_fwd_qbf16(const void* q, const int8_t* k_i8, const float* k_scale, const uint8_t* v_fp8_t,
+                                const float* v_scale, int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
+                                float softmax_scale, void* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ __all__ = [
     "sage_workspace_bytes", "sage_quant_v_scratch_bytes", "sage_quant_qk", "sage_quant_v",
     "sage_attn_fwd", "sage_attention", "sage_debug_qk_scores", "v_key_order",
     "SAGE_SMOOTH_K", "sage_k_smooth_scratch_bytes", "sage_quant_k_smooth", "sage_attn_fwd_ex",
-    "sage_workspace_bytes_ex", "sage_attention_ex",
+    "sage_workspace_bytes_ex", "sage_attention_ex", "sage_attn_fwd_qbf16",
 ]
 
 SAGE_SMOOTH_K = 1
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         "sage_quant_k_smooth": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p, p, sz, p]),
         "sage_attn_fwd_ex": (ctypes.c_int, [p, p, p, p, p, p, i64, i64, i64, i64, i64, f32, p, p, p]),
         "sage_workspace_bytes_ex": (sz, [i64, i64, i64, i64, i64]),
+        "sage_attn_fwd_qbf16": (ctypes.c_int, [p, p, p, p, p, i64, i64, i64, i64, i64, f32, p, p, p]),
         "sage_attention_ex": (ctypes.c_int, [p, p, p, i64, i64, i64, i64, i64, f32, ctypes.c_uint, p, p, p,
                                              sz, p]),
     }
@@ -341,4 +342,33 @@ def sage_attention_ex(q, k, v, softmax_scale=None, flags=0, out=None, lse=None, 
     _check(lib().sage_attention_ex(_ptr(q), _ptr(k), _ptr(v), B, Sq, Skv, H, D, float(softmax_scale),
                                    int(flags), _ptr(out), _ptr(lse), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def sage_attn_fwd_qbf16(q, k_i8, k_scale, v_fp8_t, v_scale, Skv=None, softmax_scale=None, out=None, lse=None,
+                        return_lse=False, stream=None):
+    """Attention with bf16 Q [B, Sq, H, D] quantized inside the kernel and
+    quantized K/V (Skv keys; default Sq). Returns out, or (out, lse)."""
+    torch = _torch()
+    _require(q, torch.bfloat16, "q")
+    B, Sq, H, D = _shape_bshd(q)
+    Skv = Sq if Skv is None else int(Skv)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    Skp = sage_seq_pad(Skv)
+    checks = [(k_i8, B * H * Skp * D, torch.int8), (v_fp8_t, B * H * D * Skp, torch.uint8),
+              (k_scale, B * H * (Skp // 32), torch.float32), (v_scale, B * H * D, torch.float32),
+              (out, B * Sq * H * D, torch.bfloat16)]
+    if lse is not None:
+        checks.append((lse, B * H * Sq, torch.float32))
+    for t, n, dt in checks:
+        _require(t, dt, "tensor")
+        if t.numel() < n:
+            raise ValueError("buffer too small for the given sizes")
+    _check(lib().sage_attn_fwd_qbf16(_ptr(q), _ptr(k_i8), _ptr(k_scale), _ptr(v_fp8_t), _ptr(v_scale), B, Sq, Skv,
+                                     H, D, float(softmax_scale), _ptr(out), _ptr(lse), _stream_ptr(stream)))
     return (out, lse) if lse is not None else out

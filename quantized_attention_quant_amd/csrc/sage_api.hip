@@ -178,7 +178,18 @@ sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, int64_t
   return launched("sage_quant_v");
 }
 
-sage_status attn_impl(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks,
+template <int kD, bool kQuantQ>
+void launch_attn(const int8_t* q8, const float* qs, const void* qraw, const int8_t* k8, const float* ks,
+                 const uint8_t* vt, const float* vs, int64_t Sq, int64_t Skv, int64_t H, int nqt, int64_t nwg,
+                 float c, float log2_448, void* out, float* lse, hipStream_t st) {
+  hipLaunchKernelGGL((sage::attn_fwd_kernel<kD, kQuantQ>), dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st,
+                     q8, qs, (const uint16_t*)qraw, k8, ks, vt, vs, (int)Sq, (int)Skv, (int)H, (int)seq_pad(Sq),
+                     (int)seq_pad(Skv), nqt, (int)nwg, c, log2_448, (uint16_t*)out, lse);
+}
+
+// Fused attention. Q comes either quantized (q8, qs) or, when qraw is not
+// NULL, as bf16 [B, Sq, H, D] that the kernel quantizes itself.
+sage_status attn_impl(const int8_t* q8, const float* qs, const void* qraw, const int8_t* k8, const float* ks,
                       const uint8_t* vt, const float* vs, int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
                       float softmax_scale, void* out, float* lse, hipStream_t st) {
   const int nqt = (int)((Sq + sage::kQueryTile - 1) / sage::kQueryTile);
@@ -186,14 +197,13 @@ sage_status attn_impl(const int8_t* q8, const float* qs, const int8_t* k8, const
   if (nwg > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
   const float c = (float)softmax_scale * (float)1.4426950408889634;  // fl32(fl32(scale) * fl32(log2 e))
   const float log2_448 = (float)std::log2(448.0);
-  if (D == 64)
-    hipLaunchKernelGGL(sage::attn_fwd_kernel<64>, dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st, q8, qs, k8,
-                       ks, vt, vs, (int)Sq, (int)Skv, (int)H, (int)seq_pad(Sq), (int)seq_pad(Skv), nqt, (int)nwg, c,
-                       log2_448, (uint16_t*)out, lse);
-  else
-    hipLaunchKernelGGL(sage::attn_fwd_kernel<128>, dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st, q8, qs,
-                       k8, ks, vt, vs, (int)Sq, (int)Skv, (int)H, (int)seq_pad(Sq), (int)seq_pad(Skv), nqt, (int)nwg,
-                       c, log2_448, (uint16_t*)out, lse);
+  if (D == 64) {
+    if (qraw) launch_attn<64, true>(q8, qs, qraw, k8, ks, vt, vs, Sq, Skv, H, nqt, nwg, c, log2_448, out, lse, st);
+    else launch_attn<64, false>(q8, qs, qraw, k8, ks, vt, vs, Sq, Skv, H, nqt, nwg, c, log2_448, out, lse, st);
+  } else {
+    if (qraw) launch_attn<128, true>(q8, qs, qraw, k8, ks, vt, vs, Sq, Skv, H, nqt, nwg, c, log2_448, out, lse, st);
+    else launch_attn<128, false>(q8, qs, qraw, k8, ks, vt, vs, Sq, Skv, H, nqt, nwg, c, log2_448, out, lse, st);
+  }
   return launched("sage_attn_fwd");
 }
 
@@ -293,8 +303,8 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
   if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
     return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite and >= 0");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, S, H, D, softmax_scale, out, nullptr,
-                   (hipStream_t)stream);
+  return attn_impl(q_i8, q_scale, nullptr, k_i8, k_scale, v_fp8_t, v_scale, B, S, S, H, D, softmax_scale, out,
+                   nullptr, (hipStream_t)stream);
 }
 
 sage_status sage_attention(const void* q, const void* k, const void* v, int64_t B, int64_t S, int64_t H,
@@ -321,10 +331,13 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
   float* qs = (float*)(ws + w.qs);
   float* ks = (float*)(ws + w.ks);
   float* vs = (float*)(ws + w.vs);
-  SAGE_TRY(quant_qk_impl(q, B, S, H, D, q8, qs, st));
+  (void)q8;
+  (void)qs;
+  // Q is quantized inside the attention kernel (each wave's 32 queries are
+  // one block); K and V first, by their own kernels.
   SAGE_TRY(quant_qk_impl(k, B, S, H, D, k8, ks, st));
   SAGE_TRY(quant_v_impl(v, B, S, H, D, v8, vs, ws + w.scratch, st));
-  return attn_impl(q8, qs, k8, ks, v8, vs, B, S, S, H, D, softmax_scale, out, nullptr, st);
+  return attn_impl(nullptr, nullptr, q, k8, ks, v8, vs, B, S, S, H, D, softmax_scale, out, nullptr, st);
 }
 
 sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t B, int64_t S, int64_t H,
@@ -387,8 +400,8 @@ sage_status sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int
   if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
     return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite and >= 0");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return attn_impl(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, Sq, Skv, H, D, softmax_scale, out, lse,
-                   (hipStream_t)stream);
+  return attn_impl(q_i8, q_scale, nullptr, k_i8, k_scale, v_fp8_t, v_scale, B, Sq, Skv, H, D, softmax_scale, out,
+                   lse, (hipStream_t)stream);
 }
 
 size_t sage_workspace_bytes_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D) {
@@ -423,13 +436,33 @@ sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64
   float* qs = (float*)(ws + w.qs);
   float* ks = (float*)(ws + w.ks);
   float* vs = (float*)(ws + w.vs);
-  SAGE_TRY(quant_qk_impl(q, B, Sq, H, D, q8, qs, st));
+  (void)q8;
+  (void)qs;
   if (flags & SAGE_SMOOTH_K)
     SAGE_TRY(quant_k_smooth_impl(k, B, Skv, H, D, k8, ks, (float*)(ws + w.kmean), ws + w.scratch, st));
   else
     SAGE_TRY(quant_qk_impl(k, B, Skv, H, D, k8, ks, st));
   SAGE_TRY(quant_v_impl(v, B, Skv, H, D, v8, vs, ws + w.scratch, st));
-  return attn_impl(q8, qs, k8, ks, v8, vs, B, Sq, Skv, H, D, softmax_scale, out, lse, st);
+  return attn_impl(nullptr, nullptr, q, k8, ks, v8, vs, B, Sq, Skv, H, D, softmax_scale, out, lse, st);
+}
+
+sage_status sage_attn_fwd_qbf16(const void* q, const int8_t* k_i8, const float* k_scale, const uint8_t* v_fp8_t,
+                                const float* v_scale, int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D,
+                                float softmax_scale, void* out, float* lse, void* stream) {
+  SAGE_TRY(check_shape(B, Sq, H, D));
+  SAGE_TRY(check_shape(B, Skv, H, D));
+  SAGE_TRY(check_ptr(q, "q"));
+  SAGE_TRY(check_ptr(k_i8, "k_i8"));
+  SAGE_TRY(check_ptr(k_scale, "k_scale"));
+  SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
+  SAGE_TRY(check_ptr(v_scale, "v_scale"));
+  SAGE_TRY(check_ptr(out, "out"));
+  if (lse && (((uintptr_t)lse) & 3)) return fail(SAGE_ERR_ALIGN, "lse is not 4-byte aligned");
+  if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
+    return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite and >= 0");
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  return attn_impl(nullptr, nullptr, q, k_i8, k_scale, v_fp8_t, v_scale, B, Sq, Skv, H, D, softmax_scale, out, lse,
+                   (hipStream_t)stream);
 }
 
 }  // extern "C"

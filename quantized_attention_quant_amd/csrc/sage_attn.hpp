@@ -72,6 +72,61 @@ __device__ __forceinline__ void load_q_frag(const int8_t* __restrict__ qrow, v4i
   for (int s = 0; s < kD / 32; ++s) qf[s] = *(const v4i*)(qrow + 16 * s);
 }
 
+// The same fragment computed from bf16 Q inside the attention kernel: the
+// wave's 32 query rows [q0, q0 + 32) are exactly one quantization block, so
+// the block's amax is a wave maximum. Arithmetic as quant_qk_kernel (scale =
+// fl32(amax/127), codes = clamp(rint(fl32(x * fl32(127/amax))), +-127), rows
+// >= Sq count as zeros), hence the same codes and scale bit for bit.
+template <int kD>
+__device__ __forceinline__ void quant_q_frag(const uint16_t* __restrict__ qraw, int64_t b, int h, int H, int Sq,
+                                             int row, int g, v4i qf[kD / 32], float& qs) {
+  constexpr int kVals = kD / 2;       // values of the row this lane holds
+  float x[kVals];
+  if (row < Sq) {
+    const uint16_t* src = qraw + ((b * Sq + row) * H + h) * kD + kVals * g;
+#pragma unroll
+    for (int i = 0; i < kVals / 8; ++i) {
+      const uint4 w = *(const uint4*)(src + 8 * i);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * i + 2 * j] = bf16_to_f32(ws[j] & 0xFFFFu);
+        x[8 * i + 2 * j + 1] = bf16_to_f32(ws[j] >> 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVals; ++i) x[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kVals; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = wave_max(amax);
+  float scale = 0.0f, inv = 0.0f;
+  if (amax > 0.0f) {
+    inv = __fdiv_rn(127.0f, amax);
+    scale = __fdiv_rn(amax, 127.0f);
+    if (!isfinite(inv)) { inv = 0.0f; scale = 0.0f; }
+  }
+#pragma unroll
+  for (int sidx = 0; sidx < kD / 32; ++sidx) {
+    int wd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float y = __builtin_rintf(x[16 * sidx + 4 * k + e] * inv);
+        y = fminf(fmaxf(y, -127.0f), 127.0f);
+        word |= ((uint32_t)((int)y) & 0xFFu) << (8 * e);
+      }
+      wd[k] = (int)word;
+    }
+    qf[sidx] = (v4i){wd[0], wd[1], wd[2], wd[3]};
+  }
+  qs = scale;
+}
+
 // S^T for the 128 keys of the staged tile against the wave's 32 queries:
 // sacc[u] covers keys [32 u, 32 u + 32) of the tile; every accumulator
 // starts from `init`.
@@ -280,9 +335,10 @@ __device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int
 // wave's vector work fills the cycles between them. Interval i reads K tiles i, i+1 and V tiles i-1, i,
 // and loads K tile i+2 and V tile i+1 into the third slot of each
 // three-stage LDS ring.
-template <int kD>
+template <int kD, bool kQuantQ>
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qscale,
+                     const uint16_t* __restrict__ qraw,
                      const int8_t* __restrict__ k8, const float* __restrict__ kscale,
                      const uint8_t* __restrict__ v8t, const float* __restrict__ vscale, int Sq, int Skv,
                      int H, int Sq_pad, int Skv_pad, int nqt, int num_wg, float c, float log2_448,
@@ -352,9 +408,16 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   load_v(0, 0);
   if (T > 1) load_k(1, 1);
 
+  // The wave's Q fragment and block scale: from the quantized tensors, or
+  // (kQuantQ) quantized here from bf16 Q.
   v4i qf[kD / 32];
-  load_q_frag<kD>(q8 + ((bh * Sq_pad + q0 + li) * kD + (kD / 2) * g), qf);
-  const float qs = qscale[bh * (Sq_pad / kQBlock) + q0 / kQBlock];
+  float qs;
+  if (kQuantQ) {
+    quant_q_frag<kD>(qraw, bh / H, (int)(bh % H), H, Sq, q0 + li, g, qf, qs);
+  } else {
+    load_q_frag<kD>(q8 + ((bh * Sq_pad + q0 + li) * kD + (kD / 2) * g), qf);
+    qs = qscale[bh * (Sq_pad / kQBlock) + q0 / kQBlock];
+  }
 
   v16i bias;
 #pragma unroll

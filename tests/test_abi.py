@@ -142,6 +142,19 @@ def test_extended_entry_points_validation():
     assert _call("sage_attention_ex", f, f, f, 1, 300, 77, 2, 128, fl, 0, f, z, p(FAKE + 64), ws, z) == ERR_ALIGN
 
 
+def test_attn_fwd_qbf16_validation():
+    p = ctypes.c_void_p
+    f, m, z = p(FAKE), p(MISALIGNED), p(0)
+    fl = ctypes.c_float(0.1)
+    args = [f, f, f, f]
+    assert _call("sage_attn_fwd_qbf16", z, *args, 1, 300, 77, 2, 128, fl, f, z, z) == ERR_NULL
+    assert _call("sage_attn_fwd_qbf16", m, *args, 1, 300, 77, 2, 128, fl, f, z, z) == ERR_ALIGN
+    assert _call("sage_attn_fwd_qbf16", f, *args, 1, 300, 77, 2, 96, fl, f, z, z) == ERR_UNSUP
+    assert _call("sage_attn_fwd_qbf16", f, *args, 1, 300, 0, 2, 128, fl, f, z, z) == ERR_SHAPE
+    assert _call("sage_attn_fwd_qbf16", f, *args, 1, 300, 77, 2, 128, ctypes.c_float(-1.0), f, z, z) == ERR_SHAPE
+    assert _call("sage_attn_fwd_qbf16", f, *args, 1, 300, 77, 2, 128, fl, f, p(FAKE + 1), z) == ERR_ALIGN
+
+
 def test_forced_launch_failure_hook(monkeypatch):
     monkeypatch.setenv("SAGE_TEST_FAIL_LAUNCH", "1")
     p = ctypes.c_void_p
@@ -155,6 +168,7 @@ def test_forced_launch_failure_hook(monkeypatch):
     nb = sage.sage_k_smooth_scratch_bytes(1, 300, 2, 128)
     assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, f, f, f, f, nb, z) == ERR_HIP
     assert _call("sage_attn_fwd_ex", f, f, f, f, f, f, 1, 300, 77, 2, 128, ctypes.c_float(0.1), f, f, z) == ERR_HIP
+    assert _call("sage_attn_fwd_qbf16", f, f, f, f, f, 1, 300, 77, 2, 128, ctypes.c_float(0.1), f, f, z) == ERR_HIP
     # validation still runs first
     assert _call("sage_quant_qk", f, 1, 256, 2, 96, f, f, z) == ERR_UNSUP
     assert _call("sage_quant_qk", f, 1, 256, 2, 64, f, f, z) == ERR_HIP

@@ -194,3 +194,25 @@ def test_attention_ex_lse_full_size_sampled():
         g = out[b, torch.as_tensor(rows, device=DEV), h, :].float().cpu().numpy()
         gate(g, ro, None, f"(b,h)=({b},{h}) rows={len(rows)}")
         lse_gate(lse[b, h, torch.as_tensor(rows, device=DEV)].cpu().numpy(), rl, f"(b,h)=({b},{h})")
+
+
+# --------------------------------------------------------------------------
+# Q quantized inside the attention kernel
+
+@pytest.mark.parametrize("D,Sq,Skv,H", [(128, 1, 1, 2), (128, 33, 300, 2), (128, 1000, 1000, 3), (64, 300, 77, 2),
+                                        (64, 256, 256, 1)])
+def test_attn_fwd_qbf16_equals_split_path(D, Sq, Skv, H):
+    _say(f"attn_fwd_qbf16 D={D} Sq={Sq} Skv={Skv} vs quant_qk + attn_fwd_ex")
+    q, _, _ = workloads.generate(3, S=Sq, H=H, B=1, seed=70 + Sq)
+    _, k, v = workloads.generate(3, S=Skv, H=H, B=1, seed=170 + Skv)
+    q, k, v = (np.ascontiguousarray(x[..., :D]) for x in (q, k, v))
+    scale = 1.0 / math.sqrt(D)
+    qd = to_dev(q)
+    q8, qs = sage.sage_quant_qk(qd)
+    k8, ks = sage.sage_quant_qk(to_dev(k))
+    v8, vs = sage.sage_quant_v(to_dev(v))
+    a, la = sage.sage_attn_fwd_ex(q8, qs, k8, ks, v8, vs, 1, Sq, Skv, H, D, scale, return_lse=True)
+    b, lb = sage.sage_attn_fwd_qbf16(qd, k8, ks, v8, vs, Skv=Skv, softmax_scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(la, lb)
