@@ -71,11 +71,17 @@ sage_status launched(const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int64_t v_nchunk(int64_t S) { return (S + sage::kVChunkRows - 1) / sage::kVChunkRows; }
+// V amax chunks: rows of at least kVChunkRows per chunk, at most 32 chunks
+// per (b, h) (the quantize kernel reduces them per workgroup).
+int64_t v_nchunk(int64_t S) {
+  const int64_t n = (S + sage::kVChunkRows - 1) / sage::kVChunkRows;
+  return n < 32 ? n : 32;
+}
+int64_t v_chunk_rows(int64_t S) { return (S + v_nchunk(S) - 1) / v_nchunk(S); }
 
 size_t v_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
-  // partial maxima [B*H, nchunk, D] + reciprocals [B*H, D]
-  return align256((size_t)(B * H * v_nchunk(S) * D) * 4) + align256((size_t)(B * H * D) * 4);
+  // partial maxima [B*H, nchunk, D]
+  return align256((size_t)(B * H * v_nchunk(S) * D) * 4);
 }
 
 struct Workspace {
@@ -155,13 +161,11 @@ sage_status quant_k_smooth_impl(const void* k, int64_t B, int64_t S, int64_t H, 
 
 template <int kD>
 void launch_quant_v(const void* v, int64_t S, int64_t H, int64_t Sp, int nchunk, int64_t BH, float* partial,
-                    float* vinv, float* vs, uint8_t* vt, hipStream_t st) {
+                    float* vs, uint8_t* vt, hipStream_t st) {
   hipLaunchKernelGGL(sage::v_amax_partial_kernel<kD>, dim3(nchunk, (unsigned)BH), dim3(256), 0, st,
-                     (const uint16_t*)v, (int)S, (int)H, nchunk, partial);
-  hipLaunchKernelGGL(sage::v_scale_kernel<kD>, dim3((unsigned)BH), dim3(kD), 0, st, (const float*)partial, nchunk,
-                     vs, vinv);
+                     (const uint16_t*)v, (int)S, (int)H, nchunk, (int)v_chunk_rows(S), partial);
   hipLaunchKernelGGL(sage::v_quant_kernel<kD>, dim3((unsigned)(Sp / 128), (unsigned)BH), dim3(2 * kD), 0, st,
-                     (const uint16_t*)v, (int)S, (int)H, (int)Sp, (const float*)vinv, vt);
+                     (const uint16_t*)v, (int)S, (int)H, (int)Sp, (const float*)partial, nchunk, vs, vt);
 }
 
 sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, int64_t D, uint8_t* vt, float* vs,
@@ -172,9 +176,8 @@ sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, int64_t
   // B*H goes in grid.y (limit 65535 on HIP)
   if (BH > 65535) return fail(SAGE_ERR_SHAPE, "B*H above 65535 unsupported");
   float* partial = (float*)scratch;
-  float* vinv = (float*)((char*)scratch + align256((size_t)(BH * nchunk * D) * 4));
-  if (D == 64) launch_quant_v<64>(v, S, H, Sp, nchunk, BH, partial, vinv, vs, vt, st);
-  else launch_quant_v<128>(v, S, H, Sp, nchunk, BH, partial, vinv, vs, vt, st);
+  if (D == 64) launch_quant_v<64>(v, S, H, Sp, nchunk, BH, partial, vs, vt, st);
+  else launch_quant_v<128>(v, S, H, Sp, nchunk, BH, partial, vs, vt, st);
   return launched("sage_quant_v");
 }
 

@@ -327,8 +327,10 @@ __device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int
 // one) and a vector phase (online softmax). Between two barriers, waves 0-3
 // run vector then matrix phase and waves 4-7 matrix then vector phase, so
 // that on each SIMD one wave's exp/FMA work meets the other wave's MFMAs:
-//   interval i, waves 0-3: softmax(i), PV(i), QK(i+1)
-//   interval i, waves 4-7: PV(i-1), QK(i), softmax(i)
+//   interval i, waves 0-3: softmax(i), QK(i+1), PV(i)
+//   interval i, waves 4-7: QK(i), PV(i-1), softmax(i)
+// (QK first, so that the row maxima of the new scores can be formed while
+// the PV MFMAs run)
 // (waves 0-3 compute QK(0) before interval 0; waves 4-7 compute PV(T-1)
 // after the last one). The matrix phase runs at raised wave priority
 // (s_setprio 2): its few MFMA and LDS issues then go first, and the other
@@ -444,8 +446,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
       load_v(i + 1, (sl + 1) % 3);
       vector_phase<kD, false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
       __builtin_amdgcn_s_setprio(2);
-      pv_tile<kD>(lds_v[sl], pop, li, g, o);
       qk_tile<kD>(lds_k[(sl + 1) % 3], qf, li, g, bias, s);
+      pv_tile<kD>(lds_v[sl], pop, li, g, o);
       __builtin_amdgcn_s_setprio(0);
       wait_tiles();
       __syncthreads();
@@ -459,8 +461,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
       if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
       load_v(i + 1, (sl + 1) % 3);
       __builtin_amdgcn_s_setprio(2);
-      if (i > 0) pv_tile<kD>(lds_v[(sl + 2) % 3], pop, li, g, o);
       qk_tile<kD>(lds_k[sl], qf, li, g, bias, s);
+      if (i > 0) pv_tile<kD>(lds_v[(sl + 2) % 3], pop, li, g, o);
       __builtin_amdgcn_s_setprio(0);
       vector_phase<kD, false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
       wait_tiles();

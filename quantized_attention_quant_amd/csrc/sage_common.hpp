@@ -14,7 +14,7 @@ constexpr int kAttnWaves = 8;     // waves per attention workgroup
 constexpr int kQueryTile = 32 * kAttnWaves;     // BM: queries per workgroup
 constexpr int kDebugRows = 128;                 // query rows per debug-dump workgroup
 constexpr int kVGroup = 64;       // keys per permuted group of the V^T layout
-constexpr int kVChunkRows = 512;  // rows per partial-amax chunk of V
+constexpr int kVChunkRows = 512;  // minimum rows per partial-amax chunk of V
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));

@@ -81,12 +81,12 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
   if (lane == 0) xscale[bh * nbp + t] = scale;
 }
 
-// Partial per-channel amax of |V| over a chunk of kVChunkRows rows.
+// Partial per-channel amax of |V| over a chunk of chunk_rows rows.
 // grid (nchunk, B*H), 256 threads: with G = kD/8 channel groups, thread t
 // covers channels [8 (t%G), +8) of rows t/G + (256/G) i.
 template <int kD>
 __global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __restrict__ v, int S,
-                                                             int H, int nchunk,
+                                                             int H, int nchunk, int chunk_rows,
                                                              float* __restrict__ partial) {
   constexpr int kGroups = kD / 8, kRowSets = 256 / kGroups;
   __shared__ float red[kRowSets][kD];
@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __r
   const int64_t b = bh / H;
   const int cg = threadIdx.x % kGroups, ro = threadIdx.x / kGroups;
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int rbeg = chunk * kVChunkRows;
-  const int rend = min(S, rbeg + kVChunkRows);
+  const int rbeg = chunk * chunk_rows;
+  const int rend = min(S, rbeg + chunk_rows);
   for (int row = rbeg + ro; row < rend; row += kRowSets) {
     const uint4 w = *(const uint4*)(v + (((b * S + row) * H + h) * kD + cg * 8));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -118,26 +118,6 @@ __global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __r
   }
 }
 
-// Per-channel amax over all chunks -> v_scale and the fp32 reciprocal.
-// grid B*H, kD threads (one per channel).
-template <int kD>
-__global__ __launch_bounds__(128) void v_scale_kernel(const float* __restrict__ partial, int nchunk,
-                                                      float* __restrict__ vscale,
-                                                      float* __restrict__ vinv) {
-  const int64_t bh = blockIdx.x;
-  const int c = threadIdx.x;
-  float amax = 0.0f;
-  for (int i = 0; i < nchunk; ++i) amax = fmaxf(amax, partial[(bh * nchunk + i) * kD + c]);
-  float scale = 0.0f, inv = 0.0f;
-  if (amax > 0.0f) {
-    inv = __fdiv_rn(448.0f, amax);
-    scale = __fdiv_rn(amax, 448.0f);
-    if (!isfinite(inv)) { inv = 0.0f; scale = 0.0f; }
-  }
-  vscale[bh * kD + c] = scale;
-  vinv[bh * kD + c] = inv;
-}
-
 // Quantize 128 keys x 128 channels of V to E4M3FN and write them transposed
 // ([channel][key]) with keys permuted inside each 64-key group.
 // grid (S_pad/128, B*H), 2 kD threads. Thread t covers channels
@@ -146,13 +126,37 @@ __global__ __launch_bounds__(128) void v_scale_kernel(const float* __restrict__ 
 // slot 32 (m%2) + 16u + 4 (m/2) + e, so quads m = g + 4pr and g + 4pr + 2
 // fill slots [32g + 16u + 8pr, +8). The 16 threads of a channel group write
 // one 128-byte row of the LDS tile between them.
+// Each workgroup first reduces the per-chunk maxima of its (b, h) to the
+// channel amax (at most 32 chunks) and forms scale = fl32(amax/448) and
+// inv = fl32(448/amax) (0 for amax = 0 or a non-finite reciprocal); the
+// workgroups of key tile 0 store the scales.
 template <int kD>
 __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict__ v, int S, int H,
-                                                      int S_pad, const float* __restrict__ vinv,
-                                                      uint8_t* __restrict__ vt) {
+                                                      int S_pad, const float* __restrict__ partial, int nchunk,
+                                                      float* __restrict__ vscale, uint8_t* __restrict__ vt) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kD][128 + 16];
+  __shared__ float red[2][kD];
   const int k0 = blockIdx.x * 128;
   const int64_t bh = blockIdx.y;
+  {
+    const int c = threadIdx.x % kD, half = threadIdx.x / kD;
+    float m = 0.0f;
+    for (int i = half; i < nchunk; i += 2) m = fmaxf(m, partial[(bh * nchunk + i) * kD + c]);
+    red[half][c] = m;
+    __syncthreads();
+    if (threadIdx.x < kD) {
+      const float amax = fmaxf(red[0][c], red[1][c]);
+      float scale = 0.0f, inv = 0.0f;
+      if (amax > 0.0f) {
+        inv = __fdiv_rn(448.0f, amax);
+        scale = __fdiv_rn(amax, 448.0f);
+        if (!isfinite(inv)) { inv = 0.0f; scale = 0.0f; }
+      }
+      red[0][c] = inv;
+      if (blockIdx.x == 0) vscale[bh * kD + c] = scale;
+    }
+    __syncthreads();
+  }
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
   const int run = threadIdx.x & 15, cg = threadIdx.x >> 4;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
   const int slot = 64 * grp + 32 * g + 16 * u + 8 * pr;
   float inv[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) inv[j] = vinv[bh * kD + cg * 8 + j];
+  for (int j = 0; j < 8; ++j) inv[j] = red[0][cg * 8 + j];
   float y[8][8];   // [key][channel]
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
