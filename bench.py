@@ -131,8 +131,8 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the path runs on a single MI355X and "
-              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the path runs on a single MI355X; the sharded "
+              "multi-GPU design is described but not run (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
