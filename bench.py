@@ -11,8 +11,10 @@ Output: one JSON line. ``value`` is the effective throughput of the whole
 step, 4*B*H*S^2*D / (time per step), in TOPS. The ``roofline`` object covers
 the dominant kernel (the attention kernel, entry point sage_attn_fwd_qbf16):
 its launches are bracketed by HIP events
-on the stream they run on, inside the timed region. ``cpu_baseline`` times
-the CPU oracle on a bounded sample of the same workload.
+on the stream they run on, inside the timed region. ``valu_issue`` puts the
+same launches against the vector-ALU issue rate, the limit the softmax
+arithmetic sets (instruction counts from the committed counter summary).
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -32,8 +34,11 @@ if ROOT not in sys.path:
 
 MFMA_PEAK_TOPS = 5000.0          # MI355X dense INT8 / FP8 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+# wave64 VALU issue: 256 CUs x 4 SIMDs, one instruction per SIMD per 4 cycles at 2.4 GHz
+VALU_ISSUE_PEAK_G = 1024 * 2.4e9 / 4 / 1e9
 CONFIG_INDEX = 3
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_image_dit_2048_traffic.txt")
+VALU_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_image_dit_2048_valu.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_quant_amd", "csrc", n)
                   for n in ("sage_attn.hpp", "sage_common.hpp")]
 
@@ -46,13 +51,13 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per attn_fwd launch from the committed counter summary, or
-    None when it is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_PROFILE):
+def profile_values(path, keys):
+    """Per-launch figures ``keys`` from a committed counter summary, or None
+    when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_PROFILE) as fh:
+    with open(path) as fh:
         for line in fh:
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
@@ -60,9 +65,28 @@ def measured_traffic():
     if vals.get("kernel_hash") != kernel_hash():
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return [float(vals[k]) for k in keys]
     except (KeyError, ValueError):
         return None
+
+
+def measured_traffic():
+    """HBM bytes per attn_fwd launch (calibrated FETCH_SIZE + WRITE_SIZE)."""
+    v = profile_values(TRAFFIC_PROFILE, ["hbm_bytes_per_launch"])
+    return None if v is None else v[0]
+
+
+def valu_issue(attn_ms):
+    """VALU issue slots per second of the attention launches against the
+    issue peak: every non-MFMA VALU instruction takes one slot, v_exp_f32 two
+    (it holds the SIMD's VALU for two quad-cycles)."""
+    v = profile_values(VALU_PROFILE, ["valu_insts_per_launch", "trans_insts_per_launch"])
+    if v is None:
+        return None
+    slots = v[0] + v[1]
+    achieved = slots / (attn_ms * 1e-3) / 1e9
+    return {"achieved": round(achieved, 1), "peak": VALU_ISSUE_PEAK_G, "unit": "G issue slots/s",
+            "frac": round(achieved / VALU_ISSUE_PEAK_G, 4), "slots_per_launch": slots}
 
 
 def cpu_baseline(q, k, v, scale, bn, budget_s=15.0):
@@ -218,6 +242,7 @@ def main():
             "frac": round(achieved / MFMA_PEAK_TOPS, 4),
             "traffic": traffic,
         },
+        "valu_issue": valu_issue(attn_avg),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, scale, sage.sage_kv_tile(), args.cpu_budget)
