@@ -33,6 +33,8 @@
 // cover all 256 bytes of the banks exactly once.
 #pragma once
 
+#include <type_traits>
+
 #include "sage_common.hpp"
 
 namespace sage {
@@ -250,17 +252,21 @@ struct RowState {
 };
 
 // Vector phase of one key tile for one wave: running max, rescale of l and
-// O, P' and its FP8 codes.
+// O, P' and its FP8 codes. ks4 holds the scales of the tile's four 32-key
+// K blocks.
 template <int kD, bool kTail>
-__device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const float* __restrict__ ks4, float c,
+__device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const float4 ks4, float c,
                                              float log2_448, int nvalid, int g, RowState& st, v16f o[kD / 32],
                                              v8i pop[2]) {
   float f[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) f[u] = (qs * ks4[u]) * c;
+  for (int u = 0; u < 4; ++u) f[u] = (qs * (u == 0 ? ks4.x : u == 1 ? ks4.y : u == 2 ? ks4.z : ks4.w)) * c;
 
   // t = fl32(A f) is monotone in A for f >= 0, so the tile max is taken on
-  // the (biased) integers of each 32-key block and dequantized once.
+  // the (biased) integers of each 32-key block and dequantized once. The
+  // biased maximum read as a float is 1.5 * 2^23 + A, and subtracting
+  // 1.5 * 2^23 is exact (both lie in [2^23, 2^24)), so this gives A itself
+  // with one instruction instead of an integer subtract and a conversion.
   float tmax = -INFINITY;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -271,9 +277,9 @@ __device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const fl
       for (int r = 0; r < 16; ++r)
         if (key_of(u, r, g) >= nvalid) sm[r] = INT32_MIN;
       const int mx = max16(sm);
-      if (mx != INT32_MIN) tmax = fmaxf(tmax, (float)(mx - kScoreBias) * f[u]);
+      if (mx != INT32_MIN) tmax = fmaxf(tmax, (__int_as_float(mx) - kScoreBiasF) * f[u]);
     } else {
-      tmax = fmaxf(tmax, (float)(max16(s[u]) - kScoreBias) * f[u]);
+      tmax = fmaxf(tmax, (__int_as_float(max16(s[u])) - kScoreBiasF) * f[u]);
     }
   }
   tmax = pair_max(tmax);
@@ -424,6 +430,9 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   v16i bias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) bias[r] = kScoreBias;
+  // Opaque to the optimizer: the bias then stays in VGPRs for the whole loop
+  // instead of being copied from SGPRs before every tile (8 VALU moves).
+  asm volatile("" : "+v"(bias));
   RowState st{-INFINITY, -INFINITY, 0.0f};
   v16f o[kD / 32];
 #pragma unroll
@@ -440,39 +449,66 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   // ragged (keys >= Skv masked), has no barrier after it.
   if (lead) {
     qk_tile<kD>(lds_k[0], qf, li, g, bias, s);
-    for (int i = 0; i < T - 1; ++i) {
-      const int sl = i % 3;
+    // The K block scales of tile i + 1 are loaded during tile i, which hides
+    // the scalar-load latency. The slot of tile i is i % 3; the loop body is
+    // instantiated per slot, so ring offsets are immediates of the LDS reads
+    // rather than per-tile VALU address arithmetic.
+    float4 ksc = *(const float4*)ksb;
+    auto step = [&](int i, auto slot) {
+      constexpr int sl = decltype(slot)::value;
       if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
       load_v(i + 1, (sl + 1) % 3);
-      vector_phase<kD, false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
+      const float4 ksn = *(const float4*)(ksb + (i + 1) * (kKeyTile / kQBlock));
+      vector_phase<kD, false>(s, qs, ksc, c, log2_448, kKeyTile, g, st, o, pop);
+      ksc = ksn;
       __builtin_amdgcn_s_setprio(2);
       qk_tile<kD>(lds_k[(sl + 1) % 3], qf, li, g, bias, s);
       pv_tile<kD>(lds_v[sl], pop, li, g, o);
       __builtin_amdgcn_s_setprio(0);
       wait_tiles();
       __syncthreads();
+    };
+    int i0 = 0;
+    for (; i0 + 3 <= T - 1; i0 += 3) {
+      step(i0, std::integral_constant<int, 0>{});
+      step(i0 + 1, std::integral_constant<int, 1>{});
+      step(i0 + 2, std::integral_constant<int, 2>{});
     }
+    if (i0 < T - 1) step(i0++, std::integral_constant<int, 0>{});
+    if (i0 < T - 1) step(i0++, std::integral_constant<int, 1>{});
     const int i = T - 1;
-    vector_phase<kD, true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
+    vector_phase<kD, true>(s, qs, ksc, c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
     pv_tile<kD>(lds_v[i % 3], pop, li, g, o);
   } else {
-    for (int i = 0; i < T - 1; ++i) {
-      const int sl = i % 3;
+    // (slot-instantiated body as above; the scales of tile i load at the
+    // start of the matrix phase, well ahead of the vector phase)
+    auto step = [&](int i, auto slot) {
+      constexpr int sl = decltype(slot)::value;
       if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
       load_v(i + 1, (sl + 1) % 3);
+      const float4 ksc = *(const float4*)(ksb + i * (kKeyTile / kQBlock));
       __builtin_amdgcn_s_setprio(2);
       qk_tile<kD>(lds_k[sl], qf, li, g, bias, s);
       if (i > 0) pv_tile<kD>(lds_v[(sl + 2) % 3], pop, li, g, o);
       __builtin_amdgcn_s_setprio(0);
-      vector_phase<kD, false>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, kKeyTile, g, st, o, pop);
+      vector_phase<kD, false>(s, qs, ksc, c, log2_448, kKeyTile, g, st, o, pop);
       wait_tiles();
       __syncthreads();
+    };
+    int i0 = 0;
+    for (; i0 + 3 <= T - 1; i0 += 3) {
+      step(i0, std::integral_constant<int, 0>{});
+      step(i0 + 1, std::integral_constant<int, 1>{});
+      step(i0 + 2, std::integral_constant<int, 2>{});
     }
+    if (i0 < T - 1) step(i0++, std::integral_constant<int, 0>{});
+    if (i0 < T - 1) step(i0++, std::integral_constant<int, 1>{});
     const int i = T - 1;
     const int sl = i % 3;
     if (i > 0) pv_tile<kD>(lds_v[(sl + 2) % 3], pop, li, g, o);
     qk_tile<kD>(lds_k[sl], qf, li, g, bias, s);
-    vector_phase<kD, true>(s, qs, ksb + i * (kKeyTile / kQBlock), c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
+    const float4 ksc = *(const float4*)(ksb + i * (kKeyTile / kQBlock));
+    vector_phase<kD, true>(s, qs, ksc, c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
     pv_tile<kD>(lds_v[sl], pop, li, g, o);
   }
 
