@@ -96,7 +96,7 @@ def test_quant_bit_exact_d64(S):
 
 
 @pytest.mark.parametrize("idx,Sq,Skv,H", [(1, 256, 256, 2), (3, 129, 129, 2), (2, 300, 77, 3), (5, 64, 1000, 2),
-                                          (3, 600, 600, 1)])
+                                          (3, 600, 600, 1), (3, 200, 512, 1), (2, 100, 700, 1)])
 def test_attention_d64_full_compare(idx, Sq, Skv, H):
     _say(f"attention D=64 config {idx} Sq={Sq} Skv={Skv} H={H}")
     q, _, _ = workloads.generate(idx, S=Sq, H=H, B=1, seed=60 + Sq)

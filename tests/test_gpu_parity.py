@@ -221,8 +221,12 @@ def test_debug_scores_extreme_codes():
 # --------------------------------------------------------------------------
 # attention output
 
+# key-tile counts T = ceil(S/128) up to 6, so that the attention loop (whose
+# body is instantiated per LDS ring slot, three tiles per pass) runs every
+# remainder T - 1 mod 3 with and without a full pass before it
 @pytest.mark.parametrize("S,H,B", [(1, 1, 1), (32, 1, 1), (33, 2, 1), (127, 1, 1), (128, 1, 1), (129, 2, 1),
-                                   (200, 2, 2), (256, 2, 1), (600, 3, 1)])
+                                   (200, 2, 2), (256, 2, 1), (300, 1, 1), (385, 1, 1), (512, 2, 1), (600, 3, 1),
+                                   (700, 1, 1)])
 @pytest.mark.parametrize("recipe", [1, 3])
 def test_attention_small_full_compare(S, H, B, recipe):
     _say(f"attention S={S} H={H} B={B} recipe {recipe}")
