@@ -98,13 +98,26 @@ __global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __r
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int rbeg = chunk * chunk_rows;
   const int rend = min(S, rbeg + chunk_rows);
-  for (int row = rbeg + ro; row < rend; row += kRowSets) {
-    const uint4 w = *(const uint4*)(v + (((b * S + row) * H + h) * kD + cg * 8));
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  // four rows per step, loads first, so that four 16-byte loads per thread
+  // are in flight
+  constexpr int kUnroll = 4;
+  const uint16_t* base = v + ((b * S) * H + h) * kD + cg * 8;
+  const int64_t rstride = (int64_t)H * kD;
+  for (int row0 = rbeg + ro; row0 < rend; row0 += kUnroll * kRowSets) {
+    uint4 w[kUnroll];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      m[2 * j] = fmaxf(m[2 * j], fabsf(bf16_to_f32(ws[j] & 0xFFFFu)));
-      m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(bf16_to_f32(ws[j] >> 16)));
+    for (int k = 0; k < kUnroll; ++k) {
+      const int row = row0 + k * kRowSets;
+      w[k] = row < rend ? *(const uint4*)(base + row * rstride) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m[2 * j] = fmaxf(m[2 * j], fabsf(bf16_to_f32(ws[j] & 0xFFFFu)));
+        m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf(bf16_to_f32(ws[j] >> 16)));
+      }
     }
   }
 #pragma unroll
