@@ -48,3 +48,24 @@ def test_profile_from_another_kernel_source_is_ignored(tmp_path):
 def test_profile_summaries_state_their_command(name):
     text = open(os.path.join(ROOT, "profiles", name)).read()
     assert "rocprofv3" in text and "bench.py" in text
+
+
+@pytest.mark.gpu
+def test_bench_prints_one_json_line_with_the_contract_keys():
+    import json
+    print("bench.py --steps 2 --warmup 1 --no-cpu-baseline", flush=True)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "2", "--warmup", "1",
+                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "valu_issue"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1
+    assert d["value"] > 0 and d["config"]["workload"]
+    roof = d["roofline"]
+    assert roof["bound"] == "mfma" and roof["peak"] == 5000.0
+    assert 0 < roof["frac"] < 1 and roof["traffic"] is not None
+    assert d["valu_issue"] is not None and 0 < d["valu_issue"]["frac"] < 1
