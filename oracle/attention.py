@@ -15,35 +15,31 @@ Readings taken where the pages are silent, in step order:
 1. Scores A = q8 . k8^T are exact integers (|A| <= 128*127^2 < 2^24).
 2. Dequantization in the log2 domain: c = fl32(fl32(softmax_scale) *
    fl32(log2 e)), f = fl32(fl32(q_scale * k_scale) * c) per (query block,
-   key block), t = fl32(float(A) * f).
+   key block), t = fl32(A * f).
 3. Online softmax over consecutive key tiles of ``bn`` keys, in key order (a
    flash-style forward streams K/V tiles; the tile width is the kernel's and
    is passed in). Per query row and tile tau:
    m_tau = max(m_{tau-1}, max_{j in tau} t_j)  (m_0 = -inf).
 4. P with the fixed 448 scale, folded into the exponent: m2_tau =
-   fl32(m_tau - fl32(log2 448)). The score enters the exponent as the fp32
-   value X_j = 1.5 * 2^23 + A_j (exact, since |A| < 2^21: the integer
-   accumulation starts from the bit pattern of 1.5 * 2^23, so it can be read
-   as a float directly); with F = fl32(1.5 * 2^23 * f) and C_tau =
-   fl32(F + m2_tau), arg_j = fl32(X_j * f - C_tau) (the exact real value
-   rounded once, i.e. a fused multiply-add). Mathematically arg_j = A_j f -
-   m2_tau; the two fp32 roundings in C_tau move it by at most about one unit
-   of A_j * f. P'_j = fl32(2^arg_j), so P'_j = 448 * 2^(t_j - m_tau) up to
-   rounding. p8_j = E4M3FN(P'_j) (saturating at 448). The row sum l
-   accumulates the fp32 P'_j.
+   fl32(m_tau - fl32(log2 448)); arg_j = fl32(A_j * f - m2_tau), the exact
+   real value rounded once (one fused multiply-add: the fp32 evaluation with
+   the fewest roundings; the two-step fl32(t_j - m2_tau) differs from it by
+   at most half an ulp of t_j); P'_j = fl32(2^arg_j), so P'_j = 448 *
+   2^(t_j - m_tau) up to rounding. p8_j = E4M3FN(P'_j) (saturating at 448).
+   The row sum l accumulates the fp32 P'_j.
 5. Across tiles, partial sums are combined with the factors 2^(m2_tau -
-   m2_T) of the final tile T (here in float64; the kernel rescales its fp32
+   m2_T) of the final tile T (here in float64; a kernel rescales its fp32
    accumulators as it goes, which agrees to fp32 rounding).
 6. PV: acc[c] = sum_j dec(p8_j) * dec(v8[j, c]); products of two FP8 values
    are exact. Epilogue: O[c] = bf16(acc[c] * v_scale[c] / l), formed in
    float64 and rounded once.
 
-Step 4's fused multiply-add is evaluated in float64: X * f is exact there
-(48 significant bits), and so is the subtraction of C_tau whenever the two
-terms are within a factor two of each other (the usual case, as both are near
-1.5 * 2^23 * f); otherwise the float64 result is rounded a second time to
-fp32, which disagrees with a single rounding only when the first lands
-exactly on an fp32 midpoint.
+Step 4's fused multiply-add is evaluated in float64: A * f is exact there (at
+most 21 + 24 significant bits), and so is the subtraction of m2 unless |m2|
+exceeds |A * f| by more than a factor 2^8; then the float64 result is rounded
+a second time to fp32, which differs from a single rounding only when the
+float64 value lands exactly on an fp32 midpoint. ``exponent_arg`` holds this
+step alone.
 """
 from __future__ import annotations
 
@@ -56,7 +52,6 @@ from .quant import QK_BLOCK, quant_k_smooth, quant_qk, quant_v
 
 LOG2E = np.float32(math.log2(math.e))
 LOG2_448 = np.float32(math.log2(448.0))
-SCORE_BIAS = 12582912.0          # 1.5 * 2^23
 
 
 def exp2_scale(softmax_scale: float) -> np.float32:
@@ -88,7 +83,17 @@ def _combine(shifts, l_parts, acc_parts, D, with_shift=False):
     return (acc, l, final) if with_shift else (acc, l)
 
 
-def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None, with_shift: bool = False):
+def exponent_arg(A, f, m2):
+    """Step 4's exponent: fl32(A * f - m2) with one rounding.
+
+    A: int64 [R, n] scores; f: float32 [R, n] factors; m2: fp32 values [R].
+    """
+    x = np.asarray(A, dtype=np.int64).astype(np.float64) * np.asarray(f, dtype=np.float32).astype(np.float64)
+    return f32(x - np.asarray(m2, dtype=np.float32).astype(np.float64)[:, None])
+
+
+def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None, with_shift: bool = False,
+                      trace: list | None = None):
     """Steps 2-5 for a set of query rows: the method's tile-scheduled online
     softmax with FP8 P, followed by PV.
 
@@ -98,17 +103,16 @@ def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None, with_shif
     bn:   key tile width; keys at index >= n_valid are masked.
     Returns (acc float64 [R, D], l float64 [R]); the output is
     acc * v_scale / l. With ``with_shift`` also m2 of the last tile (float64
-    holding fp32 values): l = sum_j 2^(t_j - m2_T) up to rounding.
+    holding fp32 values): l = sum_j 2^(t_j - m2_T) up to rounding. With a
+    ``trace`` list, one dict per tile (j0, j1, m2, arg, p, p8) is appended
+    to it (used by the tests that pin the exponent step).
     """
     A = np.asarray(A, dtype=np.int64)
     f = np.asarray(f, dtype=np.float32)
     R, S = A.shape
     if n_valid is None:
         n_valid = S
-    f64 = f.astype(np.float64)
-    x = A.astype(np.float64) * f64                       # A * f, exact
-    X = (A + int(SCORE_BIAS)).astype(np.float64)         # 1.5 * 2^23 + A, exact
-    F = (np.float32(SCORE_BIAS) * f).astype(np.float32)  # fl32(1.5 * 2^23 * f)
+    x = A.astype(np.float64) * f.astype(np.float64)     # A * f, exact
     m_prev = np.full(R, -np.inf)
     shifts, l_parts, acc_parts = [], [], []
     for j0 in range(0, min(S, n_valid), bn):
@@ -116,10 +120,12 @@ def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None, with_shif
         t = f32(x[:, j0:j1])                             # fl32(A * f)
         m = np.maximum(m_prev, t.max(axis=1).astype(np.float64))
         m2 = (m.astype(np.float32) - LOG2_448).astype(np.float32)
-        C = (F[:, j0:j1] + m2[:, None]).astype(np.float32)          # fl32(F + m2)
-        arg = f32(X[:, j0:j1] * f64[:, j0:j1] - C.astype(np.float64))  # fma
+        arg = exponent_arg(A[:, j0:j1], f[:, j0:j1], m2)  # fl32(A * f - m2)
         p = f32(np.exp2(arg.astype(np.float64)))         # P' in fp32
-        p_used = fp8_e4m3fn_decode(fp8_e4m3fn_encode(p))  # dec(E4M3FN(P'))
+        p8 = fp8_e4m3fn_encode(p)
+        p_used = fp8_e4m3fn_decode(p8)                   # dec(E4M3FN(P'))
+        if trace is not None:
+            trace.append(dict(j0=j0, j1=j1, m2=m2, arg=arg, p=p, p8=p8))
         shifts.append(m2.astype(np.float64))
         l_parts.append(p.astype(np.float64).sum(axis=1))
         acc_parts.append(p_used @ np.asarray(vals[j0:j1], dtype=np.float64))

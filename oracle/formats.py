@@ -13,6 +13,8 @@ to zero is kept (-0 is code 0x80).
 """
 from __future__ import annotations
 
+from fractions import Fraction
+
 import numpy as np
 
 E4M3_MAX = 448.0
@@ -99,3 +101,30 @@ def bf16_round_f64(x) -> np.ndarray:
     val = np.where(val >= 2.0 ** 128, np.inf, val)
     out = np.where(neg, -val, val)
     return out.astype(np.float32)
+
+
+def round_fraction_to_f32(fr: Fraction) -> np.float32:
+    """Nearest IEEE binary32 value to a rational number (ties to even).
+
+    Exact: the rational is compared against powers of two and divided by the
+    ulp of its binade with integer arithmetic; subnormals keep the spacing
+    2^-149. Magnitudes beyond the binary32 range are not expected here.
+    """
+    fr = Fraction(fr)
+    if fr == 0:
+        return np.float32(0.0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 23)
+    n = a / ulp
+    q = n.numerator // n.denominator
+    rem = n - q
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    return np.float32(float(sign * q * ulp))

@@ -22,14 +22,16 @@ Readings taken where the pages are silent:
 K smoothing (``k_mean``, ``quant_k_smooth``) is the option InvokeAI PR #9657
 measures on and off (sections "How it works" and "QA Instructions"); the
 pages do not define it. Reading: K - mean_s(K) per (batch, head, channel),
-quantized like K; the fp32 summation order of the mean is fixed in
-``k_mean`` so that the INT8 codes are reproducible bit for bit.
+quantized like K, where the mean is the exact mean of the (bf16) values
+rounded once to fp32, so that it and the INT8 codes are unique.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .formats import fp8_e4m3fn_encode
+from fractions import Fraction
+
+from .formats import fp8_e4m3fn_encode, round_fraction_to_f32
 
 QK_BLOCK = 32
 INT8_MAX = np.float32(127.0)
@@ -96,28 +98,48 @@ def quant_v(v: np.ndarray):
     return v8, vscale
 
 
-def k_mean(k: np.ndarray) -> np.ndarray:
-    """Per-(b, h, channel) mean of K over the sequence, in fp32.
+def _exact_sums(x: np.ndarray):
+    """Exact sums along axis 1 of a float32 [C, S] array, as (num, e): the
+    sum of row c is num[c] * 2^e[c] with Python integers num[c].
 
-    k: float32 [B, S, H, D] holding bfloat16 values. Reading of the summation
-    order: within each 32-row block the rows are added one at a time in
-    increasing s (fp32, starting from 0); the block sums are then added one
-    at a time in block order; mean = fl32(sum / S).
-    Returns float32 [B, H, D].
+    Every float32 value is M * 2^E with an integer |M| < 2^24; the values of
+    a row are brought to the row's smallest E and added as integers (int64
+    when the shifted magnitudes cannot overflow it, Python integers
+    otherwise), so no rounding happens anywhere.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    C, S = x.shape
+    mant, ex = np.frexp(x)
+    M = np.rint(mant * 2.0 ** 24).astype(np.int64)      # exact
+    E = ex.astype(np.int64) - 24
+    E = np.where(M == 0, np.iinfo(np.int64).max, E)
+    E0 = E.min(axis=1)
+    E0 = np.where(E0 == np.iinfo(np.int64).max, 0, E0)
+    shift = np.where(M == 0, 0, E - E0[:, None])
+    headroom = 62 - 24 - int(np.ceil(np.log2(max(S, 2))))
+    nums = []
+    for c in range(C):
+        if shift[c].max() <= headroom:
+            nums.append(int(np.sum(M[c] << shift[c])))
+        else:
+            nums.append(sum(int(m) << int(s) for m, s in zip(M[c], shift[c])))
+    return nums, [int(e) for e in E0]
+
+
+def k_mean(k: np.ndarray) -> np.ndarray:
+    """Per-(b, h, channel) mean of K over the sequence: the exact mean of the
+    values, rounded once to fp32 (nearest, ties to even).
+
+    k: float32 [B, S, H, D] holding bfloat16 values. Returns float32 [B, H, D].
     """
     k = np.asarray(k, dtype=np.float32)
     B, S, H, D = k.shape
-    nb = (S + QK_BLOCK - 1) // QK_BLOCK
-    x = np.zeros((B, H, nb * QK_BLOCK, D), dtype=np.float32)
-    x[:, :, :S, :] = k.transpose(0, 2, 1, 3)
-    blocks = x.reshape(B, H, nb, QK_BLOCK, D)
-    bsum = np.zeros((B, H, nb, D), dtype=np.float32)
-    for r in range(QK_BLOCK):                      # rows of a block, in order
-        bsum = (bsum + blocks[:, :, :, r, :]).astype(np.float32)
-    total = np.zeros((B, H, D), dtype=np.float32)
-    for t in range(nb):                            # blocks, in order
-        total = (total + bsum[:, :, t, :]).astype(np.float32)
-    return (total / np.float32(S)).astype(np.float32)
+    rows = np.ascontiguousarray(k.transpose(0, 2, 3, 1)).reshape(B * H * D, S)
+    nums, exps = _exact_sums(rows)
+    out = np.empty(B * H * D, dtype=np.float32)
+    for c, (n, e) in enumerate(zip(nums, exps)):
+        out[c] = round_fraction_to_f32(Fraction(n) * Fraction(2) ** e / S)
+    return out.reshape(B, H, D)
 
 
 def quant_k_smooth(k: np.ndarray):

@@ -1,8 +1,11 @@
 """Pins for the oracle's extensions: K smoothing, the log-sum-exp output and
 query/key sequences of different lengths (cross-attention).
 
-* k_mean: within the fp32 summation bound of the float64 mean; exact for
-  constant channels and for rows that cancel in pairs;
+* k_mean: equal to the exact rational mean rounded once to fp32 (brute
+  force with ``fractions.Fraction``, including channels whose values span
+  more binades than an int64 holds); exact for constant channels and for
+  rows that cancel in pairs; planted mistakes (a sequential fp32 sum, a
+  divisor of S + 1) fail it;
 * K smoothing: a zero-mean K quantizes exactly as without smoothing; a
   shifted K gives the same smoothed codes as the unshifted one when the
   shift is exactly representable; smoothed quantized attention stays
@@ -12,16 +15,21 @@ query/key sequences of different lengths (cross-attention).
 * LSE: the exact-reference LSE equals scipy's logsumexp; the oracle's LSE
   equals the fp64 logsumexp of the dequantized scores within the bound of
   its fp32 exponent roundings; one key gives closed forms for O and LSE;
+  planted mistakes (no ln 2, an offset) fail it;
 * cross-attention: close to exact fp64 attention for Sq != Skv with ragged
   tails on both sides; Sq = Skv reproduces the self-attention call.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
 from scipy.special import logsumexp
 
+import oracle.attention as oatt
+import oracle.quant as oquant
 import workloads
+from fp_exact import round_fraction_to_f32
 from oracle import (
     attention_head,
     exact_attention_fp64,
@@ -52,16 +60,48 @@ def _cross_inputs(idx, Sq, Skv, H=2, seed=5):
 
 # ---------------------------------------------------------------- k_mean
 
-@pytest.mark.parametrize("S", [1, 31, 32, 100, 777])
-def test_k_mean_within_fp32_summation_bound(S):
+def _brute_mean(k):
+    B, S, H, D = k.shape
+    out = np.empty((B, H, D), dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            for c in range(D):
+                tot = sum(Fraction(float(x)) for x in k[b, :, h, c])
+                out[b, h, c] = float(round_fraction_to_f32(tot / S))
+    return out
+
+
+def _mean_inputs(S):
     k = workloads.generate_custom((1, S, 3, 128), seed=S, kind="normal", scale=3.0)
     k[:, :, 1, 5] += np.float32(40.0)          # a channel with an offset
-    m = k_mean(k)
-    exact = k.astype(np.float64).mean(axis=1)  # [B, H, D]
-    nb = (S + 31) // 32
-    absum = np.abs(k.astype(np.float64)).sum(axis=1)
-    bound = (31 + nb + 2) * U32 * absum / S + U32 * np.abs(exact) + 1e-30
-    assert np.all(np.abs(m.astype(np.float64) - exact) <= bound)
+    k[:, :, 2, 9] = np.float32(2.0 ** -30)     # values 50 binades apart in one
+    k[:, ::7, 2, 9] = np.float32(2.0 ** 22)    # channel: the Python-integer path
+    return workloads.bf16_round(k)
+
+
+@pytest.mark.parametrize("S", [1, 31, 32, 100, 777])
+def test_k_mean_is_the_exact_mean_rounded_once(S):
+    k = _mean_inputs(S)
+    assert np.array_equal(k_mean(k).view(np.uint32), _brute_mean(k).view(np.uint32))
+
+
+def test_planted_k_mean_mistakes_fail_the_pin(monkeypatch):
+    k = _mean_inputs(777)
+    ref = _brute_mean(k)
+
+    def sequential_fp32(kk):                    # fp32 running sum over s
+        acc = np.zeros((kk.shape[0], kk.shape[2], kk.shape[3]), np.float32)
+        for s_ in range(kk.shape[1]):
+            acc = (acc + kk[:, s_]).astype(np.float32)
+        return (acc / np.float32(kk.shape[1])).astype(np.float32)
+
+    real = oquant.k_mean
+
+    def off_by_one(kk):                         # divides by S + 1
+        return (real(kk).astype(np.float64) * kk.shape[1] / (kk.shape[1] + 1)).astype(np.float32)
+
+    for mistake in (sequential_fp32, off_by_one):
+        assert not np.array_equal(mistake(k), ref), mistake.__name__
 
 
 def test_k_mean_constant_channels_exact():
@@ -73,7 +113,7 @@ def test_k_mean_constant_channels_exact():
 
 
 def test_zero_mean_k_quantizes_as_unsmoothed():
-    # rows in cancelling pairs: every running fp32 sum returns to exactly 0
+    # rows in cancelling pairs: the exact mean is 0
     half = workloads.generate_custom((1, 48, 2, 128), seed=9, kind="normal", scale=2.0)
     k = np.empty((1, 96, 2, 128), dtype=np.float32)
     k[:, 0::2] = half
@@ -150,6 +190,16 @@ def test_oracle_lse_matches_dequantized_logsumexp(idx, Sq, Skv):
         tmax = np.abs(deq).max(axis=1) * cfg.softmax_scale * math.log2(math.e)
         bound = math.log(2.0) * (2.5 * fmax + 8 * U32 * (tmax + 30)) + 4 * U32 * np.abs(ref)
         assert np.all(np.abs(lse.astype(np.float64) - ref) <= bound), h
+
+
+def test_planted_lse_mistakes_fail_the_pin(monkeypatch):
+    real = oatt.lse_from_state
+    for mistake in (lambda m2, l: np.float32(1.0 / math.log(2.0)) * real(m2, l) * np.float32(math.log(2.0) ** 2),
+                    lambda m2, l: oatt.f32(np.asarray(m2, np.float64) + np.log2(np.asarray(l, np.float64))),
+                    lambda m2, l: real(m2, l) + np.float32(0.01)):
+        monkeypatch.setattr(oatt, "lse_from_state", mistake)
+        with pytest.raises(AssertionError):
+            test_oracle_lse_matches_dequantized_logsumexp(1, 256, 256)
 
 
 def test_single_key_closed_forms():
