@@ -131,11 +131,9 @@ sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t
  *   A = q8 . k8^T (exact int32);  c = fl32(fl32(softmax_scale)*fl32(log2 e));
  *   f = fl32(fl32(q_scale*k_scale)*c) per (query block, key block);
  *   t = fl32(A*f); m = running max of t (keys >= S masked);
- *   m2 = fl32(m - fl32(log2 448)); with X = 1.5*2^23 + A (the int32
- *   accumulator starts from the bit pattern of 1.5*2^23, so it reads as this
- *   exact float) and C = fl32(fl32(1.5*2^23*f) + m2):
- *   P' = 2^fl32(X*f - C) (fused multiply-add, hardware exp2), which is
- *   448 * 2^(t - m) up to rounding;
+ *   m2 = fl32(m - fl32(log2 448)); P' = 2^fl32(A*f - m2), the exponent
+ *   being the exact real value A*f - m2 rounded once (a fused multiply-add;
+ *   hardware exp2), so P' = 448 * 2^(t - m) up to rounding;
  *   l = sum of fp32 P' (rescaled by 2^(m2_old - m2) when the max moves);
  *   p8 = E4M3FN(min(P', 448)); acc[c] = sum p8 * v8[c] (FP8 MFMA, fp32
  *   accumulation, same rescaling); out = bf16_rne(acc * v_scale[c] / l).
@@ -179,7 +177,7 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
 /* Flags of sage_attention_ex. */
 #define SAGE_SMOOTH_K 1u  /* quantize K - mean_s(K) instead of K (sage_quant_k_smooth) */
 
-/* Bytes of scratch sage_quant_k_smooth needs (per-block channel sums). */
+/* Bytes of scratch sage_quant_k_smooth needs (fp64 per-block channel sums). */
 size_t sage_k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 
 /*
@@ -195,10 +193,12 @@ size_t sage_k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
  *            (as sage_quant_qk, applied to the smoothed values).
  *   k_mean   fp32 [B, H, D] out.
  *   scratch  device memory of sage_k_smooth_scratch_bytes(...) bytes.
- * Per channel c of (b, h): for each 32-row block t, bsum[t] = fp32 sum of
- * k[s] over the block's valid rows, added one row at a time in increasing
- * s; sum = fp32 sum of bsum[t] in increasing t; k_mean = fl32(sum / S). The
- * values quantized are fl32(k - k_mean) on rows s < S (padded rows stay 0).
+ * Per channel c of (b, h): k_mean = the exact mean of k[s] over s < S,
+ * rounded once to fp32 (nearest, ties to even). The sums are formed in fp64,
+ * which is exact while the values of a channel span fewer than about
+ * 45 - log2(S) binades (outside that range the mean may differ from the
+ * exact rounding by one ulp). The values quantized are fl32(k - k_mean) on
+ * rows s < S (padded rows stay 0).
  */
 sage_status sage_quant_k_smooth(const void* k, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* k_i8,
                                 float* k_scale, float* k_mean, void* scratch, size_t scratch_bytes,

@@ -130,8 +130,8 @@ sage_status quant_qk_impl(const void* x, int64_t B, int64_t S, int64_t H, int64_
 }
 
 size_t k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
-  // block sums [B*H, S_pad/32, D]
-  return align256((size_t)(B * H * (seq_pad(S) / sage::kQBlock) * D) * 4);
+  // fp64 block sums [B*H, S_pad/32, D]
+  return align256((size_t)(B * H * (seq_pad(S) / sage::kQBlock) * D) * 8);
 }
 
 // K smoothing: per-channel mean over S, then INT8 quantization of K - mean.
@@ -141,8 +141,8 @@ void launch_k_mean(const void* k, int64_t S, int64_t H, int nbp, int64_t total, 
   // 4 waves of 64/(kD/8) blocks each per workgroup
   const int64_t per_wg = 4 * (64 / (kD / 8));
   hipLaunchKernelGGL(sage::k_block_sum_kernel<kD>, dim3((unsigned)((total + per_wg - 1) / per_wg)), dim3(256), 0,
-                     st, (const uint16_t*)k, (int)S, (int)H, nbp, total, (float*)scratch);
-  hipLaunchKernelGGL(sage::k_mean_kernel<kD>, dim3((unsigned)BH), dim3(kD), 0, st, (const float*)scratch, nbp,
+                     st, (const uint16_t*)k, (int)S, (int)H, nbp, total, (double*)scratch);
+  hipLaunchKernelGGL(sage::k_mean_kernel<kD>, dim3((unsigned)BH), dim3(kD), 0, st, (const double*)scratch, nbp,
                      (int)S, kmean);
 }
 

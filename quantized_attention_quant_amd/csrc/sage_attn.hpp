@@ -12,8 +12,9 @@
 // The INT8 score accumulators start at 0x4B400000, the bit pattern of the
 // fp32 value 1.5 * 2^23: since |A| < 2^21, the accumulated integer
 // 0x4B400000 + A is the bit pattern of the exact fp32 value 1.5 * 2^23 + A,
-// so the scores are read as floats without a conversion instruction, and
-// integer order of the biased values is still score order.
+// and integer order of the biased values is still score order. One exact
+// subtraction recovers A as a float; the exponent A * f - m2 is then formed
+// with a single rounding (one fused multiply-add).
 //
 // Work decomposition: one workgroup = 8 waves = 256 queries of one (b, h);
 // each wave owns 32 queries and streams all keys in tiles of 128.
@@ -178,16 +179,17 @@ __device__ __forceinline__ float pair_sum(float x) {
 constexpr int kScoreBias = 0x4B400000;        // bits of 1.5 * 2^23
 constexpr float kScoreBiasF = 12582912.0f;     // 1.5 * 2^23
 
-// P' = 2^(A f - m2) for the 64 scores of a lane, their fp32 sum, and the
-// E4M3FN codes packed in the FP8 MFMA B-operand order (byte 16 (u%2) + r of
-// pop[u/2] holds sub-tile u, register r). With X = 1.5 * 2^23 + A (the biased
-// accumulator read as a float) the exponent is fl32(X f - nc[u]) with
-// nc[u] = fl32(fl32(1.5 * 2^23 * f) + m2), one fused multiply-add.
+// P' = 2^fl32(A f - m2) for the 64 scores of a lane, their fp32 sum, and
+// the E4M3FN codes packed in the FP8 MFMA B-operand order (byte 16 (u%2) + r
+// of pop[u/2] holds sub-tile u, register r). A is read from the biased
+// accumulator X = 1.5 * 2^23 + A as the exact difference X - 1.5 * 2^23; the
+// exponent is then one fused multiply-add, i.e. the exact A f - m2 rounded
+// once.
 // kClamp: saturate before the conversion (the hardware conversion gives NaN
 // above 464). kTail: keys at or past `nvalid` get P' = 0.
 template <bool kClamp, bool kTail>
-__device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], const float nc[4], int nvalid,
-                                           int g, v8i pop[2]) {
+__device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], float m2, int nvalid, int g,
+                                           v8i pop[2]) {
   // eight independent partial sums keep the additions off the critical path
   float ls[8];
 #pragma unroll
@@ -198,7 +200,8 @@ __device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], co
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * j + e;
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(s[u][r]), f[u], -nc[u]));
+        const float a = __int_as_float(s[u][r]) - kScoreBiasF;   // exact
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(a, f[u], -m2));
         if (kTail && key_of(u, r, g) >= nvalid) pe = 0.0f;
         const int k = 4 * (j & 1) + e;
         ls[k] = (u == 0 && j < 2) ? pe : ls[k] + pe;
@@ -286,22 +289,16 @@ __device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const fl
   const float m_new = fmaxf(st.m, tmax);
   const float m2_new = m_new - log2_448;
   const float alpha = __builtin_amdgcn_exp2f(st.m2 - m2_new);
-  float nc[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) nc[u] = kScoreBiasF * f[u] + m2_new;
   float lsum;
   // P' of the largest score is 448 * 2^e, where e collects the fp32
-  // roundings of m, m2, 1.5 * 2^23 * f and nc. While all of those stay below
-  // 2^17 in magnitude each rounding is at most 2^-7 and P' <= 448 * 2^(1/32)
+  // roundings of m, m2 and the exponent: at most half an ulp of m and of m2
+  // plus 2^-21. While |m| < 2^17 that is below 2^-5 and P' < 448 * 2^(1/32)
   // < 464, the limit of the conversion (above it the hardware gives NaN).
-  // Larger values (outlier-scale Q/K blocks) take the saturating variant.
-  float mag = fabsf(m_new);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) mag = fmaxf(mag, fabsf(nc[u]));
-  if (__builtin_expect(__ballot(mag >= 131072.0f) != 0, 0))
-    lsum = softmax_p<true, kTail>(s, f, nc, nvalid, g, pop);
+  // Larger maxima (outlier-scale Q/K blocks) take the saturating variant.
+  if (__builtin_expect(__ballot(fabsf(m_new) >= 131072.0f) != 0, 0))
+    lsum = softmax_p<true, kTail>(s, f, m2_new, nvalid, g, pop);
   else
-    lsum = softmax_p<false, kTail>(s, f, nc, nvalid, g, pop);
+    lsum = softmax_p<false, kTail>(s, f, m2_new, nvalid, g, pop);
   st.l = st.l * alpha + lsum;
   if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll

@@ -208,14 +208,18 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
     *(uint4*)(dst + 16 * q) = *(const uint4*)(&tile[c][64 * half + 16 * q]);
 }
 
-// K smoothing, step 1: per (b, h, 32-row block) fp32 sum of each channel,
-// rows added one at a time in increasing s (rows >= S contribute nothing).
+// K smoothing, step 1: per (b, h, 32-row block) sum of each channel in
+// fp64 (rows >= S contribute nothing). bf16 values have 8 significant bits,
+// so these sums, and the sums of step 2, are exact in fp64 whenever the
+// values of a channel span fewer than 53 - 8 - log2(S) binades (for S =
+// 75600 and values of magnitude above 2^-20 times the channel's largest,
+// always).
 // With L = kD/8 lanes per block, 64/L blocks per wave: lane l covers
 // channels [8 (l%L), +8) of block (64/L) (4 blockIdx + wave) + l/L.
 template <int kD>
 __global__ __launch_bounds__(256) void k_block_sum_kernel(const uint16_t* __restrict__ k, int S, int H,
                                                           int nbp, int64_t total_blocks,
-                                                          float* __restrict__ partial) {
+                                                          double* __restrict__ partial) {
   constexpr int kLanesPerBlock = kD / 8, kBlocksPerWave = 64 / kLanesPerBlock;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t blk = ((int64_t)blockIdx.x * 4 + wave) * kBlocksPerWave + lane / kLanesPerBlock;
@@ -225,33 +229,49 @@ __global__ __launch_bounds__(256) void k_block_sum_kernel(const uint16_t* __rest
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
   const int col = (lane % kLanesPerBlock) * 8;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const int rend = min(S, (t + 1) * kQBlock);
   for (int row = t * kQBlock; row < rend; ++row) {
     const uint4 w = *(const uint4*)(k + (((b * S + row) * H + h) * kD + col));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc[2 * j] = acc[2 * j] + bf16_to_f32(ws[j] & 0xFFFFu);
-      acc[2 * j + 1] = acc[2 * j + 1] + bf16_to_f32(ws[j] >> 16);
+      acc[2 * j] += (double)bf16_to_f32(ws[j] & 0xFFFFu);
+      acc[2 * j + 1] += (double)bf16_to_f32(ws[j] >> 16);
     }
   }
-  float4* dst = (float4*)(partial + blk * kD + col);
-  dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  double2* dst = (double2*)(partial + blk * kD + col);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dst[j] = make_double2(acc[2 * j], acc[2 * j + 1]);
 }
 
-// K smoothing, step 2: the block sums added in block order, then
-// mean = fl32(sum / S). grid B*H, kD threads (one per channel).
+// fp32 value nearest to sum / n (ties to even) for an exact fp64 sum: the
+// fp64 quotient is correctly rounded, so it can only be wrong for fp32 when
+// it lands exactly on the midpoint of two fp32 values; then the sign of the
+// exact remainder sum - q n (one fp64 fused multiply-add) decides.
+__device__ __forceinline__ float div_round_f32(double sum, double n) {
+  const double q = sum / n;
+  const float f0 = (float)q;
+  if ((double)f0 == q) return f0;
+  const float nb = q > (double)f0 ? nextafterf(f0, INFINITY) : nextafterf(f0, -INFINITY);
+  if (q != 0.5 * ((double)f0 + (double)nb)) return f0;
+  const double r = __builtin_fma(-q, n, sum);
+  if (r == 0.0) return f0;                 // a true tie: f0 is the even one
+  const bool up = r > 0.0;                 // the exact quotient lies above q
+  return (up == ((double)nb > (double)f0)) ? nb : f0;
+}
+
+// K smoothing, step 2: the block sums added in fp64, then mean =
+// fl32(sum / S) with one rounding. grid B*H, kD threads (one per channel).
 template <int kD>
-__global__ __launch_bounds__(128) void k_mean_kernel(const float* __restrict__ partial, int nbp, int S,
+__global__ __launch_bounds__(128) void k_mean_kernel(const double* __restrict__ partial, int nbp, int S,
                                                      float* __restrict__ kmean) {
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
-  const float* p = partial + bh * (int64_t)nbp * kD + c;
-  float sum = 0.0f;
-  for (int t = 0; t < nbp; ++t) sum = sum + p[(int64_t)t * kD];
-  kmean[bh * kD + c] = __fdiv_rn(sum, (float)S);
+  const double* p = partial + bh * (int64_t)nbp * kD + c;
+  double sum = 0.0;
+  for (int t = 0; t < nbp; ++t) sum += p[(int64_t)t * kD];
+  kmean[bh * kD + c] = div_round_f32(sum, (double)S);
 }
 
 }  // namespace sage

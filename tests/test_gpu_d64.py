@@ -14,54 +14,18 @@ import workloads
 
 torch = pytest.importorskip("torch")
 sage = pytest.importorskip("quantized_attention_quant_amd")
+from gpu_common import DEV, gate, kappa, lse_gate, say, to_dev  # noqa: E402
 
 pytestmark = pytest.mark.gpu
-
-DEV = "cuda"
 D = 64
 SCALE = 1.0 / math.sqrt(D)
 
 
-def _say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
-
-def to_dev(a):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(DEV)
+_say = say
 
 
 def d64(x):
     return np.ascontiguousarray(x[..., :D])
-
-
-def cosine(a, b):
-    a = np.asarray(a, np.float64).ravel()
-    b = np.asarray(b, np.float64).ravel()
-    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
-
-
-def gate(got, ref, exact=None, label=""):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert np.all(np.isfinite(got)), label
-    err = np.max(np.abs(got - ref))
-    c = cosine(got, ref)
-    _say(f"  {label}: max|err| {err:.4g} (bound {1e-2 * np.max(np.abs(ref)):.4g}), cosine {c:.7f}")
-    assert err <= 1e-2 * np.max(np.abs(ref)), label
-    assert c >= 0.9999, label
-    if exact is not None:
-        assert cosine(got, exact) >= 0.99, label
-
-
-def lse_gate(got, ref, label=""):
-    err = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
-    assert np.all(err <= 4e-5 + 1e-6 * np.abs(ref)), label
-
-
-def kappa(p):
-    g, u, r = p // 32, (p // 16) % 2, p % 16
-    return 32 * u + 8 * (r // 4) + 4 * g + (r % 4)
 
 
 @pytest.mark.parametrize("S", [1, 33, 300, 1000])

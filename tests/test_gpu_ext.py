@@ -2,13 +2,7 @@
 K smoothing (codes, scales and the K mean bit-exact), the log-sum-exp output
 and query/key sequences of different lengths (cross-attention).
 
-Output gate as in test_gpu_parity: max|O_gpu - O_oracle| <= 1e-2 max|O_oracle|,
-cosine >= 0.9999, and cosine >= 0.99 against exact fp64 attention.
-LSE gate: |lse_gpu - lse_oracle| <= 4e-5 + 1e-6 |lse_oracle|. The two sides
-differ by fp32 summation order in l (at most a few hundred roundings along
-a row's chain, each 2^-24 relative: <= 2e-5 in ln l), the hardware log2
-(about 1 ulp) and the final fp32 roundings of m2 + log2 l and of the
-product with ln 2.
+Output and LSE gates as stated in gpu_common.
 """
 import math
 import sys
@@ -21,49 +15,11 @@ import workloads
 
 torch = pytest.importorskip("torch")
 sage = pytest.importorskip("quantized_attention_quant_amd")
+from gpu_common import DEV, gate, lse_gate, say, to_dev  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-DEV = "cuda"
-
-
-def _say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
-
-def to_dev(a):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).to(DEV)
-
-
-def cosine(a, b):
-    a = np.asarray(a, np.float64).ravel()
-    b = np.asarray(b, np.float64).ravel()
-    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
-
-
-def gate(got, ref, exact=None, label=""):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert np.all(np.isfinite(got)), label
-    err = np.max(np.abs(got - ref))
-    c = cosine(got, ref)
-    _say(f"  {label}: max|err| {err:.4g} (bound {1e-2 * np.max(np.abs(ref)):.4g}), cosine {c:.7f}"
-         + (f", cos vs fp64 {cosine(got, exact):.5f}" if exact is not None else ""))
-    assert err <= 1e-2 * np.max(np.abs(ref)), label
-    assert c >= 0.9999, label
-    if exact is not None:
-        assert cosine(got, exact) >= 0.99, label
-
-
-def lse_gate(got, ref, label=""):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert np.all(np.isfinite(got)), label
-    err = np.abs(got - ref)
-    bound = 4e-5 + 1e-6 * np.abs(ref)
-    _say(f"  {label}: lse max|err| {err.max():.3g} (bound at that row {bound.ravel()[err.argmax()]:.3g})")
-    assert np.all(err <= bound), label
+_say = say
 
 
 def cross_inputs(idx, Sq, Skv, H, seed):
