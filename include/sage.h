@@ -122,6 +122,29 @@ sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t
                          uint8_t* v_fp8_t, float* v_scale, void* scratch, size_t scratch_bytes,
                          void* stream);
 
+/* Size of the static device buffer sage_quant_v_noalloc uses (8 MiB per GPU). */
+#define SAGE_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * sage_quant_v_noalloc - sage_quant_v without a scratch argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same arguments,
+ * layouts, results and errors as sage_quant_v, except:
+ *   - the per-chunk partial maxima live in a static device buffer of
+ *     SAGE_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from the
+ *     first call on that GPU until the process ends; shapes whose scratch
+ *     (sage_quant_v_scratch_bytes) exceeds it return SAGE_ERR_WORKSPACE;
+ *   - the call allocates and frees nothing; its first call on a device
+ *     looks up the buffer's device address (hipGetSymbolAddress), on the
+ *     current device, which must be the device of `stream`;
+ *   - every call on one GPU shares that buffer: calls that may overlap on
+ *     one GPU (different streams, no ordering between them) race and must
+ *     be serialized by the caller. Each call overwrites all of the scratch
+ *     it reads, so no state carries from one call to the next.
+ */
+sage_status sage_quant_v_noalloc(const void* v, int64_t B, int64_t S, int64_t H, int64_t D,
+                                 uint8_t* v_fp8_t, float* v_scale, void* stream);
+
 /*
  * sage_attn_fwd - fused attention on quantized inputs (issue #15014,
  * problem statement: INT8 QK^T and FP8 PV with FP32 accumulation).

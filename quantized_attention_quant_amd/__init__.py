@@ -20,7 +20,7 @@ __all__ = [
     "sage_workspace_bytes", "sage_quant_v_scratch_bytes", "sage_quant_qk", "sage_quant_v",
     "sage_attn_fwd", "sage_attention", "sage_debug_qk_scores", "v_key_order",
     "SAGE_SMOOTH_K", "sage_k_smooth_scratch_bytes", "sage_quant_k_smooth", "sage_attn_fwd_ex",
-    "sage_workspace_bytes_ex", "sage_attention_ex", "sage_attn_fwd_qbf16",
+    "sage_workspace_bytes_ex", "sage_attention_ex", "sage_attn_fwd_qbf16", "sage_quant_v_noalloc",
 ]
 
 SAGE_SMOOTH_K = 1
@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
         "sage_workspace_bytes": (sz, [i64, i64, i64, i64]),
         "sage_quant_qk": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p]),
         "sage_quant_v": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p, sz, p]),
+        "sage_quant_v_noalloc": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p]),
         "sage_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, i64, i64, i64, i64, f32, p, p]),
         "sage_attention": (ctypes.c_int, [p, p, p, i64, i64, i64, i64, f32, p, p, sz, p]),
         "sage_debug_qk_scores": (ctypes.c_int, [p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64,
@@ -184,6 +185,21 @@ def sage_quant_v(v, v_fp8_t=None, v_scale=None, scratch=None, stream=None):
         raise ValueError("output buffers too small")
     _check(lib().sage_quant_v(_ptr(v), B, S, H, D, _ptr(v_fp8_t), _ptr(v_scale), _ptr(scratch),
                               scratch.numel() * scratch.element_size(), _stream_ptr(stream)))
+    return v_fp8_t, v_scale
+
+
+def sage_quant_v_noalloc(v, v_fp8_t, v_scale, stream=None):
+    """sage_quant_v with its scratch in the library's static device buffer:
+    allocates nothing (outputs must be passed in). Returns (v_fp8_t, v_scale)."""
+    torch = _torch()
+    _require(v, torch.bfloat16, "v")
+    B, S, H, D = _shape_bshd(v)
+    Sp = sage_seq_pad(S)
+    _require(v_fp8_t, torch.uint8, "v_fp8_t")
+    _require(v_scale, torch.float32, "v_scale")
+    if v_fp8_t.numel() < B * H * D * Sp or v_scale.numel() < B * H * D:
+        raise ValueError("output buffers too small")
+    _check(lib().sage_quant_v_noalloc(_ptr(v), B, S, H, D, _ptr(v_fp8_t), _ptr(v_scale), _stream_ptr(stream)))
     return v_fp8_t, v_scale
 
 

@@ -7,11 +7,19 @@
 #include <cstdarg>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "sage.h"
 #include "sage_attn.hpp"
 #include "sage_common.hpp"
 #include "sage_quant.hpp"
+
+// Scratch of sage_quant_v_noalloc (the per-chunk partial maxima of V), in
+// device memory that exists from module load until the process ends, one
+// copy per GPU. Host code never passes this name to a kernel: it stands for
+// a host-side shadow, not a device address. The device address comes from
+// hipGetSymbolAddress, once per device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[SAGE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -71,6 +79,29 @@ sage_status launched(const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call per device and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sage_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SAGE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SAGE_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SAGE_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SAGE_OK;
+}
+
 // V amax chunks: rows of at least kVChunkRows per chunk, at most 32 chunks
 // per (b, h) (the quantize kernel reduces them per workgroup).
 int64_t v_nchunk(int64_t S) {
@@ -85,7 +116,7 @@ size_t v_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
 }
 
 struct Workspace {
-  size_t q8, k8, v8, qs, ks, vs, scratch, total, scratch_bytes;
+  size_t q8, k8, v8, qs, ks, vs, scratch_off, total, scratch_bytes;
 };
 
 Workspace layout(int64_t B, int64_t S, int64_t H, int64_t D) {
@@ -99,9 +130,9 @@ Workspace layout(int64_t B, int64_t S, int64_t H, int64_t D) {
   w.qs = w.v8 + qk;
   w.ks = w.qs + sc;
   w.vs = w.ks + sc;
-  w.scratch = w.vs + align256((size_t)(B * H * D) * 4);
+  w.scratch_off = w.vs + align256((size_t)(B * H * D) * 4);
   w.scratch_bytes = v_scratch_bytes(B, S, H, D);
-  w.total = w.scratch + w.scratch_bytes;
+  w.total = w.scratch_off + w.scratch_bytes;
   return w;
 }
 
@@ -136,25 +167,25 @@ size_t k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
 
 // K smoothing: per-channel mean over S, then INT8 quantization of K - mean.
 template <int kD>
-void launch_k_mean(const void* k, int64_t S, int64_t H, int nbp, int64_t total, int64_t BH, void* scratch,
+void launch_k_mean(const void* k, int64_t S, int64_t H, int nbp, int64_t total, int64_t BH, void* scratch_buf,
                    float* kmean, hipStream_t st) {
   // 4 waves of 64/(kD/8) blocks each per workgroup
   const int64_t per_wg = 4 * (64 / (kD / 8));
   hipLaunchKernelGGL(sage::k_block_sum_kernel<kD>, dim3((unsigned)((total + per_wg - 1) / per_wg)), dim3(256), 0,
-                     st, (const uint16_t*)k, (int)S, (int)H, nbp, total, (double*)scratch);
-  hipLaunchKernelGGL(sage::k_mean_kernel<kD>, dim3((unsigned)BH), dim3(kD), 0, st, (const double*)scratch, nbp,
+                     st, (const uint16_t*)k, (int)S, (int)H, nbp, total, (double*)scratch_buf);
+  hipLaunchKernelGGL(sage::k_mean_kernel<kD>, dim3((unsigned)BH), dim3(kD), 0, st, (const double*)scratch_buf, nbp,
                      (int)S, kmean);
 }
 
 sage_status quant_k_smooth_impl(const void* k, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* kq,
-                                float* ks, float* kmean, void* scratch, hipStream_t st) {
+                                float* ks, float* kmean, void* scratch_buf, hipStream_t st) {
   const int64_t Sp = seq_pad(S);
   const int nbp = (int)(Sp / sage::kQBlock);
   const int64_t total = B * H * nbp;
   const int64_t BH = B * H;
   if ((total + 15) / 16 > INT32_MAX || BH > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
-  if (D == 64) launch_k_mean<64>(k, S, H, nbp, total, BH, scratch, kmean, st);
-  else launch_k_mean<128>(k, S, H, nbp, total, BH, scratch, kmean, st);
+  if (D == 64) launch_k_mean<64>(k, S, H, nbp, total, BH, scratch_buf, kmean, st);
+  else launch_k_mean<128>(k, S, H, nbp, total, BH, scratch_buf, kmean, st);
   SAGE_TRY(launched("sage_quant_k_smooth (mean)"));
   return quant_qk_impl(k, B, S, H, D, kq, ks, st, kmean);
 }
@@ -169,13 +200,13 @@ void launch_quant_v(const void* v, int64_t S, int64_t H, int64_t Sp, int nchunk,
 }
 
 sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, int64_t D, uint8_t* vt, float* vs,
-                         void* scratch, hipStream_t st) {
+                         void* scratch_buf, hipStream_t st) {
   const int64_t Sp = seq_pad(S);
   const int nchunk = (int)v_nchunk(S);
   const int64_t BH = B * H;
   // B*H goes in grid.y (limit 65535 on HIP)
   if (BH > 65535) return fail(SAGE_ERR_SHAPE, "B*H above 65535 unsupported");
-  float* partial = (float*)scratch;
+  float* partial = (float*)scratch_buf;
   if (D == 64) launch_quant_v<64>(v, S, H, Sp, nchunk, BH, partial, vs, vt, st);
   else launch_quant_v<128>(v, S, H, Sp, nchunk, BH, partial, vs, vt, st);
   return launched("sage_quant_v");
@@ -211,7 +242,7 @@ sage_status attn_impl(const int8_t* q8, const float* qs, const void* qraw, const
 }
 
 struct WorkspaceEx {
-  size_t q8, k8, v8, qs, ks, vs, kmean, scratch, scratch_bytes, total;
+  size_t q8, k8, v8, qs, ks, vs, kmean, scratch_off, scratch_bytes, total;
 };
 
 // Intermediates of sage_attention_ex, each 256-byte aligned; the scratch
@@ -226,10 +257,10 @@ WorkspaceEx layout_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D) 
   w.ks = w.qs + align256((size_t)(B * H * (Sqp / 32)) * 4);
   w.vs = w.ks + align256((size_t)(B * H * (Skp / 32)) * 4);
   w.kmean = w.vs + align256((size_t)(B * H * D) * 4);
-  w.scratch = w.kmean + align256((size_t)(B * H * D) * 4);
+  w.scratch_off = w.kmean + align256((size_t)(B * H * D) * 4);
   const size_t a = v_scratch_bytes(B, Skv, H, D), b = k_smooth_scratch_bytes(B, Skv, H, D);
   w.scratch_bytes = a > b ? a : b;
-  w.total = w.scratch + w.scratch_bytes;
+  w.total = w.scratch_off + w.scratch_bytes;
   return w;
 }
 
@@ -280,16 +311,32 @@ sage_status sage_quant_qk(const void* x, int64_t B, int64_t S, int64_t H, int64_
 }
 
 sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t D, uint8_t* v_fp8_t,
-                         float* v_scale, void* scratch, size_t scratch_bytes, void* stream) {
+                         float* v_scale, void* scratch_buf, size_t scratch_bytes, void* stream) {
   SAGE_TRY(check_shape(B, S, H, D));
   SAGE_TRY(check_ptr(v, "v"));
   SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
   SAGE_TRY(check_ptr(v_scale, "v_scale"));
-  SAGE_TRY(check_ptr(scratch, "scratch"));
+  SAGE_TRY(check_ptr(scratch_buf, "scratch"));
   if (scratch_bytes < v_scratch_bytes(B, S, H, D))
     return fail(SAGE_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, v_scratch_bytes(B, S, H, D));
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return quant_v_impl(v, B, S, H, D, v_fp8_t, v_scale, scratch, (hipStream_t)stream);
+  return quant_v_impl(v, B, S, H, D, v_fp8_t, v_scale, scratch_buf, (hipStream_t)stream);
+}
+
+sage_status sage_quant_v_noalloc(const void* v, int64_t B, int64_t S, int64_t H, int64_t D, uint8_t* v_fp8_t,
+                                 float* v_scale, void* stream) {
+  SAGE_TRY(check_shape(B, S, H, D));
+  SAGE_TRY(check_ptr(v, "v"));
+  SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
+  SAGE_TRY(check_ptr(v_scale, "v_scale"));
+  const size_t need = v_scratch_bytes(B, S, H, D);
+  if (need > (size_t)SAGE_NOALLOC_SCRATCH_BYTES)
+    return fail(SAGE_ERR_WORKSPACE, "needs %zu bytes of scratch, above the %zu-byte static buffer (use sage_quant_v)",
+                need, (size_t)SAGE_NOALLOC_SCRATCH_BYTES);
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  void* buf = nullptr;
+  SAGE_TRY(noalloc_scratch(&buf));
+  return quant_v_impl(v, B, S, H, D, v_fp8_t, v_scale, buf, (hipStream_t)stream);
 }
 
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
@@ -339,7 +386,7 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
   // Q is quantized inside the attention kernel (each wave's 32 queries are
   // one block); K and V first, by their own kernels.
   SAGE_TRY(quant_qk_impl(k, B, S, H, D, k8, ks, st));
-  SAGE_TRY(quant_v_impl(v, B, S, H, D, v8, vs, ws + w.scratch, st));
+  SAGE_TRY(quant_v_impl(v, B, S, H, D, v8, vs, ws + w.scratch_off, st));
   return attn_impl(nullptr, nullptr, q, k8, ks, v8, vs, B, S, S, H, D, softmax_scale, out, nullptr, st);
 }
 
@@ -372,19 +419,19 @@ size_t sage_k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
 }
 
 sage_status sage_quant_k_smooth(const void* k, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* k_i8,
-                                float* k_scale, float* k_mean, void* scratch, size_t scratch_bytes,
+                                float* k_scale, float* k_mean, void* scratch_buf, size_t scratch_bytes,
                                 void* stream) {
   SAGE_TRY(check_shape(B, S, H, D));
   SAGE_TRY(check_ptr(k, "k"));
   SAGE_TRY(check_ptr(k_i8, "k_i8"));
   SAGE_TRY(check_ptr(k_scale, "k_scale"));
   SAGE_TRY(check_ptr(k_mean, "k_mean"));
-  SAGE_TRY(check_ptr(scratch, "scratch"));
+  SAGE_TRY(check_ptr(scratch_buf, "scratch"));
   if (scratch_bytes < k_smooth_scratch_bytes(B, S, H, D))
     return fail(SAGE_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes,
                 k_smooth_scratch_bytes(B, S, H, D));
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  return quant_k_smooth_impl(k, B, S, H, D, k_i8, k_scale, k_mean, scratch, (hipStream_t)stream);
+  return quant_k_smooth_impl(k, B, S, H, D, k_i8, k_scale, k_mean, scratch_buf, (hipStream_t)stream);
 }
 
 sage_status sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
@@ -442,10 +489,10 @@ sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64
   (void)q8;
   (void)qs;
   if (flags & SAGE_SMOOTH_K)
-    SAGE_TRY(quant_k_smooth_impl(k, B, Skv, H, D, k8, ks, (float*)(ws + w.kmean), ws + w.scratch, st));
+    SAGE_TRY(quant_k_smooth_impl(k, B, Skv, H, D, k8, ks, (float*)(ws + w.kmean), ws + w.scratch_off, st));
   else
     SAGE_TRY(quant_qk_impl(k, B, Skv, H, D, k8, ks, st));
-  SAGE_TRY(quant_v_impl(v, B, Skv, H, D, v8, vs, ws + w.scratch, st));
+  SAGE_TRY(quant_v_impl(v, B, Skv, H, D, v8, vs, ws + w.scratch_off, st));
   return attn_impl(nullptr, nullptr, q, k8, ks, v8, vs, B, Sq, Skv, H, D, softmax_scale, out, lse, st);
 }
 

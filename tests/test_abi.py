@@ -75,6 +75,10 @@ def test_validation_codes():
     p = ctypes.c_void_p
     f, m = p(FAKE), p(MISALIGNED)
     z = p(0)
+    # the allocation-free V quantizer: shapes beyond its static buffer
+    assert _call("sage_quant_v_noalloc", f, 1, 16384, 513, 128, f, f, z) == ERR_WS
+    assert b"static buffer" in sage.lib().sage_last_error()
+    assert _call("sage_quant_v_noalloc", z, 1, 256, 2, 128, f, f, z) == ERR_NULL
     # head dim, sizes
     assert _call("sage_quant_qk", f, 1, 256, 2, 96, f, f, z) == ERR_UNSUP
     assert _call("sage_quant_qk", f, 1, 256, 2, 256, f, f, z) == ERR_UNSUP
