@@ -27,7 +27,8 @@
  *     calls that share output or workspace buffers must be ordered by the
  *     caller.
  *   - Sizes: B, S, H >= 1, S <= 2^24, B, H <= 2^20 and B*H*S_pad*D < 2^62;
- *     larger sizes return SAGE_ERR_SHAPE.
+ *     each launch's grid (about B*H*S_pad/128 workgroups for the largest)
+ *     must also stay below 2^31. Larger sizes return SAGE_ERR_SHAPE.
  *   - Head dim: D == 128 is the pages' operation. D == 64 is also accepted
  *     by every entry point except sage_debug_qk_scores (the pages' callers
  *     fall back for it: the VAE's head dim 64, diffusers PR #15060, section
@@ -81,8 +82,10 @@ int64_t sage_seq_pad(int64_t S);
 /* Bytes of scratch sage_quant_v needs (per-chunk partial maxima). */
 size_t sage_quant_v_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 
-/* Bytes of workspace sage_attention needs: the quantized Q, K, V, their
- * scales and sage_quant_v's scratch, each 256-byte aligned. 0 on bad sizes. */
+/* Bytes of workspace sage_attention needs: the quantized K and V, their
+ * scales and sage_quant_v's scratch, each 256-byte aligned (Q needs none: the
+ * attention kernel quantizes it), about 2 bytes per element of K or V, i.e.
+ * 0.67 bytes per element of the three inputs. 0 on bad sizes. */
 size_t sage_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 
 /*
@@ -121,6 +124,17 @@ sage_status sage_quant_qk(const void* x, int64_t B, int64_t S, int64_t H, int64_
 sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t D,
                          uint8_t* v_fp8_t, float* v_scale, void* scratch, size_t scratch_bytes,
                          void* stream);
+
+/*
+ * sage_quant_kv - sage_quant_qk(K) and sage_quant_v(V) together, as the
+ * attention needs them (issue #15014, problem statement: K per 32-row block,
+ * V per channel). Same arguments, layouts, results and errors as those two
+ * calls; the first of its two launches quantizes K and takes V's per-chunk
+ * maxima in one pass over both tensors. scratch as for sage_quant_v.
+ */
+sage_status sage_quant_kv(const void* k, const void* v, int64_t B, int64_t S, int64_t H, int64_t D,
+                          int8_t* k_i8, float* k_scale, uint8_t* v_fp8_t, float* v_scale, void* scratch,
+                          size_t scratch_bytes, void* stream);
 
 /* Size of the static device buffer sage_quant_v_noalloc uses (8 MiB per GPU). */
 #define SAGE_NOALLOC_SCRATCH_BYTES (8u << 20)
@@ -167,8 +181,7 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
                           void* stream);
 
 /*
- * sage_attention - one call: sage_quant_qk(K), sage_quant_v(V) and the
- * attention with Q quantized inside the kernel (sage_attn_fwd_qbf16; the
+ * sage_attention - one call: sage_quant_kv(K, V) and the attention with Q quantized inside the kernel (sage_attn_fwd_qbf16; the
  * result equals sage_quant_qk(Q) followed by sage_attn_fwd), with every
  * intermediate inside the caller's workspace (>= sage_workspace_bytes(B, S, H, D) bytes, 256-byte
  * aligned). This is the gfx1201_sage_attention(q, k, v, softmax_scale)
@@ -200,7 +213,7 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
 /* Flags of sage_attention_ex. */
 #define SAGE_SMOOTH_K 1u  /* quantize K - mean_s(K) instead of K (sage_quant_k_smooth) */
 
-/* Bytes of scratch sage_quant_k_smooth needs (fp64 per-block channel sums). */
+/* Bytes of scratch sage_quant_k_smooth needs (fp64 channel sums per 256-row chunk). */
 size_t sage_k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 
 /*

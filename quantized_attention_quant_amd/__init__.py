@@ -21,6 +21,7 @@ __all__ = [
     "sage_attn_fwd", "sage_attention", "sage_debug_qk_scores", "v_key_order",
     "SAGE_SMOOTH_K", "sage_k_smooth_scratch_bytes", "sage_quant_k_smooth", "sage_attn_fwd_ex",
     "sage_workspace_bytes_ex", "sage_attention_ex", "sage_attn_fwd_qbf16", "sage_quant_v_noalloc",
+    "sage_quant_kv",
 ]
 
 SAGE_SMOOTH_K = 1
@@ -60,6 +61,7 @@ def lib() -> ctypes.CDLL:
         "sage_quant_qk": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p]),
         "sage_quant_v": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p, sz, p]),
         "sage_quant_v_noalloc": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p]),
+        "sage_quant_kv": (ctypes.c_int, [p, p, i64, i64, i64, i64, p, p, p, p, p, sz, p]),
         "sage_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, i64, i64, i64, i64, f32, p, p]),
         "sage_attention": (ctypes.c_int, [p, p, p, i64, i64, i64, i64, f32, p, p, sz, p]),
         "sage_debug_qk_scores": (ctypes.c_int, [p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64,
@@ -186,6 +188,39 @@ def sage_quant_v(v, v_fp8_t=None, v_scale=None, scratch=None, stream=None):
     _check(lib().sage_quant_v(_ptr(v), B, S, H, D, _ptr(v_fp8_t), _ptr(v_scale), _ptr(scratch),
                               scratch.numel() * scratch.element_size(), _stream_ptr(stream)))
     return v_fp8_t, v_scale
+
+
+def sage_quant_kv(k, v, k_i8=None, k_scale=None, v_fp8_t=None, v_scale=None, scratch=None, stream=None):
+    """K to INT8 and V to FP8 in one call (fused first pass).
+    Returns (k_i8, k_scale, v_fp8_t, v_scale)."""
+    torch = _torch()
+    _require(k, torch.bfloat16, "k")
+    _require(v, torch.bfloat16, "v")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, S, H, D = _shape_bshd(k)
+    Sp = sage_seq_pad(S)
+    dev = k.device
+    if k_i8 is None:
+        k_i8 = torch.empty((B, H, Sp, D), dtype=torch.int8, device=dev)
+    if k_scale is None:
+        k_scale = torch.empty((B, H, Sp // 32), dtype=torch.float32, device=dev)
+    if v_fp8_t is None:
+        v_fp8_t = torch.empty((B, H, D, Sp), dtype=torch.uint8, device=dev)
+    if v_scale is None:
+        v_scale = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    if scratch is None:
+        scratch = torch.empty(max(sage_quant_v_scratch_bytes(B, S, H, D), 256), dtype=torch.uint8, device=dev)
+    for t, n, dt, name in ((k_i8, B * H * Sp * D, torch.int8, "k_i8"), (k_scale, B * H * (Sp // 32), torch.float32,
+                           "k_scale"), (v_fp8_t, B * H * D * Sp, torch.uint8, "v_fp8_t"),
+                           (v_scale, B * H * D, torch.float32, "v_scale")):
+        _require(t, dt, name)
+        if t.numel() < n:
+            raise ValueError(f"{name} too small")
+    _check(lib().sage_quant_kv(_ptr(k), _ptr(v), B, S, H, D, _ptr(k_i8), _ptr(k_scale), _ptr(v_fp8_t),
+                               _ptr(v_scale), _ptr(scratch), scratch.numel() * scratch.element_size(),
+                               _stream_ptr(stream)))
+    return k_i8, k_scale, v_fp8_t, v_scale
 
 
 def sage_quant_v_noalloc(v, v_fp8_t, v_scale, stream=None):

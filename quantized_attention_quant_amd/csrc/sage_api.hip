@@ -115,21 +115,21 @@ size_t v_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
   return align256((size_t)(B * H * v_nchunk(S) * D) * 4);
 }
 
+// Intermediates of sage_attention, each 256-byte aligned: K codes, V codes
+// (transposed), K and V scales, and sage_quant_v's scratch. Q needs no
+// region: the attention kernel quantizes it.
 struct Workspace {
-  size_t q8, k8, v8, qs, ks, vs, scratch_off, total, scratch_bytes;
+  size_t k8, v8, ks, vs, scratch_off, total, scratch_bytes;
 };
 
 Workspace layout(int64_t B, int64_t S, int64_t H, int64_t D) {
   Workspace w{};
   const int64_t Sp = seq_pad(S);
-  const size_t qk = align256((size_t)(B * H * Sp * D));
-  const size_t sc = align256((size_t)(B * H * (Sp / 32)) * 4);
-  w.q8 = 0;
-  w.k8 = w.q8 + qk;
-  w.v8 = w.k8 + qk;
-  w.qs = w.v8 + qk;
-  w.ks = w.qs + sc;
-  w.vs = w.ks + sc;
+  const size_t codes = align256((size_t)(B * H * Sp * D));
+  w.k8 = 0;
+  w.v8 = w.k8 + codes;
+  w.ks = w.v8 + codes;
+  w.vs = w.ks + align256((size_t)(B * H * (Sp / 32)) * 4);
   w.scratch_off = w.vs + align256((size_t)(B * H * D) * 4);
   w.scratch_bytes = v_scratch_bytes(B, S, H, D);
   w.total = w.scratch_off + w.scratch_bytes;
@@ -160,56 +160,100 @@ sage_status quant_qk_impl(const void* x, int64_t B, int64_t S, int64_t H, int64_
   return launched("sage_quant_qk");
 }
 
+int64_t k_sum_chunks(int64_t S) { return (S + sage::kKSumRows - 1) / sage::kKSumRows; }
+
 size_t k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {
-  // fp64 block sums [B*H, S_pad/32, D]
-  return align256((size_t)(B * H * (seq_pad(S) / sage::kQBlock) * D) * 8);
+  // fp64 chunk sums [B*H, ceil(S/256), D]
+  return align256((size_t)(B * H * k_sum_chunks(S) * D) * 8);
 }
 
 // K smoothing: per-channel mean over S, then INT8 quantization of K - mean.
 template <int kD>
-void launch_k_mean(const void* k, int64_t S, int64_t H, int nbp, int64_t total, int64_t BH, void* scratch_buf,
+void launch_k_mean(const void* k, int64_t S, int64_t H, int nck, int64_t total, int64_t BH, void* scratch_buf,
                    float* kmean, hipStream_t st) {
-  // 4 waves of 64/(kD/8) blocks each per workgroup
+  // 4 waves of 64/(kD/8) chunks each per workgroup
   const int64_t per_wg = 4 * (64 / (kD / 8));
   hipLaunchKernelGGL(sage::k_block_sum_kernel<kD>, dim3((unsigned)((total + per_wg - 1) / per_wg)), dim3(256), 0,
-                     st, (const uint16_t*)k, (int)S, (int)H, nbp, total, (double*)scratch_buf);
-  hipLaunchKernelGGL(sage::k_mean_kernel<kD>, dim3((unsigned)BH), dim3(kD), 0, st, (const double*)scratch_buf, nbp,
+                     st, (const uint16_t*)k, (int)S, (int)H, nck, total, (double*)scratch_buf);
+  hipLaunchKernelGGL(sage::k_mean_kernel<kD>, dim3((unsigned)BH), dim3(kD), 0, st, (const double*)scratch_buf, nck,
                      (int)S, kmean);
 }
 
 sage_status quant_k_smooth_impl(const void* k, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* kq,
                                 float* ks, float* kmean, void* scratch_buf, hipStream_t st) {
-  const int64_t Sp = seq_pad(S);
-  const int nbp = (int)(Sp / sage::kQBlock);
-  const int64_t total = B * H * nbp;
+  const int nck = (int)k_sum_chunks(S);
+  const int64_t total = B * H * nck;
   const int64_t BH = B * H;
   if ((total + 15) / 16 > INT32_MAX || BH > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
-  if (D == 64) launch_k_mean<64>(k, S, H, nbp, total, BH, scratch_buf, kmean, st);
-  else launch_k_mean<128>(k, S, H, nbp, total, BH, scratch_buf, kmean, st);
+  if (D == 64) launch_k_mean<64>(k, S, H, nck, total, BH, scratch_buf, kmean, st);
+  else launch_k_mean<128>(k, S, H, nck, total, BH, scratch_buf, kmean, st);
   SAGE_TRY(launched("sage_quant_k_smooth (mean)"));
   return quant_qk_impl(k, B, S, H, D, kq, ks, st, kmean);
 }
 
+int64_t v_tiles_per_head(int64_t S) {
+  return (seq_pad(S) / 128 + sage::kVTilesPerWg - 1) / sage::kVTilesPerWg;
+}
+
+// grid sizes of the V passes (and of the fused K/V pre-pass) fit int32
+sage_status check_v_grids(int64_t B, int64_t S, int64_t H) {
+  const int64_t BH = B * H;
+  const int64_t nkwg = (B * H * (seq_pad(S) / sage::kQBlock) + 3) / 4;
+  if (BH * v_nchunk(S) + nkwg > INT32_MAX || BH * v_tiles_per_head(S) > INT32_MAX)
+    return fail(SAGE_ERR_SHAPE, "grid too large");
+  return SAGE_OK;
+}
+
 template <int kD>
-void launch_quant_v(const void* v, int64_t S, int64_t H, int64_t Sp, int nchunk, int64_t BH, float* partial,
-                    float* vs, uint8_t* vt, hipStream_t st) {
-  hipLaunchKernelGGL(sage::v_amax_partial_kernel<kD>, dim3(nchunk, (unsigned)BH), dim3(256), 0, st,
+void launch_v_quant(const void* v, int64_t S, int64_t H, int64_t BH, const float* partial, float* vs, uint8_t* vt,
+                    hipStream_t st) {
+  const int64_t nvt = v_tiles_per_head(S);
+  hipLaunchKernelGGL(sage::v_quant_kernel<kD>, dim3((unsigned)(BH * nvt)), dim3(2 * kD), 0, st, (const uint16_t*)v,
+                     (int)S, (int)H, (int)seq_pad(S), (int)nvt, partial, (int)v_nchunk(S), vs, vt);
+}
+
+template <int kD>
+void launch_quant_v(const void* v, int64_t S, int64_t H, int nchunk, int64_t BH, float* partial, float* vs,
+                    uint8_t* vt, hipStream_t st) {
+  hipLaunchKernelGGL(sage::v_amax_partial_kernel<kD>, dim3((unsigned)(BH * nchunk)), dim3(256), 0, st,
                      (const uint16_t*)v, (int)S, (int)H, nchunk, (int)v_chunk_rows(S), partial);
-  hipLaunchKernelGGL(sage::v_quant_kernel<kD>, dim3((unsigned)(Sp / 128), (unsigned)BH), dim3(2 * kD), 0, st,
-                     (const uint16_t*)v, (int)S, (int)H, (int)Sp, (const float*)partial, nchunk, vs, vt);
+  launch_v_quant<kD>(v, S, H, BH, partial, vs, vt, st);
 }
 
 sage_status quant_v_impl(const void* v, int64_t B, int64_t S, int64_t H, int64_t D, uint8_t* vt, float* vs,
                          void* scratch_buf, hipStream_t st) {
-  const int64_t Sp = seq_pad(S);
+  SAGE_TRY(check_v_grids(B, S, H));
   const int nchunk = (int)v_nchunk(S);
   const int64_t BH = B * H;
-  // B*H goes in grid.y (limit 65535 on HIP)
-  if (BH > 65535) return fail(SAGE_ERR_SHAPE, "B*H above 65535 unsupported");
   float* partial = (float*)scratch_buf;
-  if (D == 64) launch_quant_v<64>(v, S, H, Sp, nchunk, BH, partial, vs, vt, st);
-  else launch_quant_v<128>(v, S, H, Sp, nchunk, BH, partial, vs, vt, st);
+  if (D == 64) launch_quant_v<64>(v, S, H, nchunk, BH, partial, vs, vt, st);
+  else launch_quant_v<128>(v, S, H, nchunk, BH, partial, vs, vt, st);
   return launched("sage_quant_v");
+}
+
+// K quantization and V quantization with one fused first pass: one launch
+// quantizes K and takes V's per-chunk maxima, a second quantizes V.
+template <int kD>
+void launch_quant_kv(const void* k, const void* v, int64_t B, int64_t S, int64_t H, int8_t* kq, float* ks,
+                     float* partial, float* vs, uint8_t* vt, hipStream_t st) {
+  const int64_t BH = B * H;
+  const int nbp = (int)(seq_pad(S) / sage::kQBlock);
+  const int64_t total = BH * nbp;
+  const int64_t nkwg = (total + 3) / 4;
+  const int nchunk = (int)v_nchunk(S);
+  hipLaunchKernelGGL(sage::kv_prepass_kernel<kD>, dim3((unsigned)(nkwg + BH * nchunk)), dim3(256), 0, st,
+                     (const uint16_t*)k, (const uint16_t*)v, (int)S, (int)H, (int)seq_pad(S), nbp, total, (int)nkwg,
+                     kq, ks, nchunk, (int)v_chunk_rows(S), partial);
+  launch_v_quant<kD>(v, S, H, BH, partial, vs, vt, st);
+}
+
+sage_status quant_kv_impl(const void* k, const void* v, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* kq,
+                          float* ks, uint8_t* vt, float* vs, void* scratch_buf, hipStream_t st) {
+  SAGE_TRY(check_v_grids(B, S, H));
+  float* partial = (float*)scratch_buf;
+  if (D == 64) launch_quant_kv<64>(k, v, B, S, H, kq, ks, partial, vs, vt, st);
+  else launch_quant_kv<128>(k, v, B, S, H, kq, ks, partial, vs, vt, st);
+  return launched("sage_quant_kv");
 }
 
 template <int kD, bool kQuantQ>
@@ -242,19 +286,19 @@ sage_status attn_impl(const int8_t* q8, const float* qs, const void* qraw, const
 }
 
 struct WorkspaceEx {
-  size_t q8, k8, v8, qs, ks, vs, kmean, scratch_off, scratch_bytes, total;
+  size_t k8, v8, ks, vs, kmean, scratch_off, scratch_bytes, total;
 };
 
-// Intermediates of sage_attention_ex, each 256-byte aligned; the scratch
-// region serves sage_quant_v and, before it, the K-smoothing block sums.
+// Intermediates of sage_attention_ex, each 256-byte aligned (no Q region:
+// the attention kernel quantizes Q); the scratch region serves sage_quant_v
+// and, before it, the K-smoothing block sums.
 WorkspaceEx layout_ex(int64_t B, int64_t Sq, int64_t Skv, int64_t H, int64_t D) {
+  (void)Sq;
   WorkspaceEx w{};
-  const int64_t Sqp = seq_pad(Sq), Skp = seq_pad(Skv);
-  w.q8 = 0;
-  w.k8 = w.q8 + align256((size_t)(B * H * Sqp * D));
+  const int64_t Skp = seq_pad(Skv);
+  w.k8 = 0;
   w.v8 = w.k8 + align256((size_t)(B * H * Skp * D));
-  w.qs = w.v8 + align256((size_t)(B * H * Skp * D));
-  w.ks = w.qs + align256((size_t)(B * H * (Sqp / 32)) * 4);
+  w.ks = w.v8 + align256((size_t)(B * H * Skp * D));
   w.vs = w.ks + align256((size_t)(B * H * (Skp / 32)) * 4);
   w.kmean = w.vs + align256((size_t)(B * H * D) * 4);
   w.scratch_off = w.kmean + align256((size_t)(B * H * D) * 4);
@@ -323,6 +367,23 @@ sage_status sage_quant_v(const void* v, int64_t B, int64_t S, int64_t H, int64_t
   return quant_v_impl(v, B, S, H, D, v_fp8_t, v_scale, scratch_buf, (hipStream_t)stream);
 }
 
+sage_status sage_quant_kv(const void* k, const void* v, int64_t B, int64_t S, int64_t H, int64_t D, int8_t* k_i8,
+                          float* k_scale, uint8_t* v_fp8_t, float* v_scale, void* scratch_buf, size_t scratch_bytes,
+                          void* stream) {
+  SAGE_TRY(check_shape(B, S, H, D));
+  SAGE_TRY(check_ptr(k, "k"));
+  SAGE_TRY(check_ptr(v, "v"));
+  SAGE_TRY(check_ptr(k_i8, "k_i8"));
+  SAGE_TRY(check_ptr(k_scale, "k_scale"));
+  SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
+  SAGE_TRY(check_ptr(v_scale, "v_scale"));
+  SAGE_TRY(check_ptr(scratch_buf, "scratch"));
+  if (scratch_bytes < v_scratch_bytes(B, S, H, D))
+    return fail(SAGE_ERR_WORKSPACE, "scratch has %zu bytes, needs %zu", scratch_bytes, v_scratch_bytes(B, S, H, D));
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  return quant_kv_impl(k, v, B, S, H, D, k_i8, k_scale, v_fp8_t, v_scale, scratch_buf, (hipStream_t)stream);
+}
+
 sage_status sage_quant_v_noalloc(const void* v, int64_t B, int64_t S, int64_t H, int64_t D, uint8_t* v_fp8_t,
                                  float* v_scale, void* stream) {
   SAGE_TRY(check_shape(B, S, H, D));
@@ -375,18 +436,13 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
-  int8_t* q8 = (int8_t*)(ws + w.q8);
   int8_t* k8 = (int8_t*)(ws + w.k8);
   uint8_t* v8 = (uint8_t*)(ws + w.v8);
-  float* qs = (float*)(ws + w.qs);
   float* ks = (float*)(ws + w.ks);
   float* vs = (float*)(ws + w.vs);
-  (void)q8;
-  (void)qs;
-  // Q is quantized inside the attention kernel (each wave's 32 queries are
-  // one block); K and V first, by their own kernels.
-  SAGE_TRY(quant_qk_impl(k, B, S, H, D, k8, ks, st));
-  SAGE_TRY(quant_v_impl(v, B, S, H, D, v8, vs, ws + w.scratch_off, st));
+  // K and V by the fused pre-pass; Q is quantized inside the attention
+  // kernel (each wave's 32 queries are one block).
+  SAGE_TRY(quant_kv_impl(k, v, B, S, H, D, k8, ks, v8, vs, ws + w.scratch_off, st));
   return attn_impl(nullptr, nullptr, q, k8, ks, v8, vs, B, S, S, H, D, softmax_scale, out, nullptr, st);
 }
 
@@ -480,19 +536,16 @@ sage_status sage_attention_ex(const void* q, const void* k, const void* v, int64
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
-  int8_t* q8 = (int8_t*)(ws + w.q8);
   int8_t* k8 = (int8_t*)(ws + w.k8);
   uint8_t* v8 = (uint8_t*)(ws + w.v8);
-  float* qs = (float*)(ws + w.qs);
   float* ks = (float*)(ws + w.ks);
   float* vs = (float*)(ws + w.vs);
-  (void)q8;
-  (void)qs;
-  if (flags & SAGE_SMOOTH_K)
+  if (flags & SAGE_SMOOTH_K) {
     SAGE_TRY(quant_k_smooth_impl(k, B, Skv, H, D, k8, ks, (float*)(ws + w.kmean), ws + w.scratch_off, st));
-  else
-    SAGE_TRY(quant_qk_impl(k, B, Skv, H, D, k8, ks, st));
-  SAGE_TRY(quant_v_impl(v, B, Skv, H, D, v8, vs, ws + w.scratch_off, st));
+    SAGE_TRY(quant_v_impl(v, B, Skv, H, D, v8, vs, ws + w.scratch_off, st));
+  } else {
+    SAGE_TRY(quant_kv_impl(k, v, B, Skv, H, D, k8, ks, v8, vs, ws + w.scratch_off, st));
+  }
   return attn_impl(nullptr, nullptr, q, k8, ks, v8, vs, B, Sq, Skv, H, D, softmax_scale, out, lse, st);
 }
 

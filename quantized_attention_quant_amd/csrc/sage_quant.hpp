@@ -11,20 +11,15 @@
 
 namespace sage {
 
-// One wave per (b, h, 32-row block); 4 waves per workgroup; head dim kD.
-// With L = kD/8 lanes per row, lane l covers columns [8 (l%L), +8) of rows
-// (64/L) it + l/L, it = 0 .. 32 L/64 - 1.
+// INT8 quantization of one (b, h, 32-row block) `blk` by one wave; head
+// dim kD. With L = kD/8 lanes per row, lane l covers columns [8 (l%L), +8)
+// of rows (64/L) it + l/L, it = 0 .. 32 L/64 - 1.
 // kSmooth: the values quantized are fl32(x - xmean[b, h, c]) (K smoothing);
 // rows >= S stay zero.
 template <int kD, bool kSmooth>
-__global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restrict__ x, int S, int H,
-                                                       int S_pad, int nbp, int64_t total_blocks,
-                                                       const float* __restrict__ xmean,
-                                                       int8_t* __restrict__ xq,
-                                                       float* __restrict__ xscale) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + wave;
-  if (blk >= total_blocks) return;
+__device__ __forceinline__ void quant_qk_block(const uint16_t* __restrict__ x, int S, int H, int S_pad, int nbp,
+                                               int64_t blk, const float* __restrict__ xmean,
+                                               int8_t* __restrict__ xq, float* __restrict__ xscale, int lane) {
   const int t = (int)(blk % nbp);
   const int64_t bh = blk / nbp;
   const int h = (int)(bh % H);
@@ -81,17 +76,29 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
   if (lane == 0) xscale[bh * nbp + t] = scale;
 }
 
-// Partial per-channel amax of |V| over a chunk of chunk_rows rows.
-// grid (nchunk, B*H), 256 threads: with G = kD/8 channel groups, thread t
-// covers channels [8 (t%G), +8) of rows t/G + (256/G) i.
+// One wave per (b, h, 32-row block); 4 waves per workgroup.
+template <int kD, bool kSmooth>
+__global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restrict__ x, int S, int H,
+                                                       int S_pad, int nbp, int64_t total_blocks,
+                                                       const float* __restrict__ xmean,
+                                                       int8_t* __restrict__ xq,
+                                                       float* __restrict__ xscale) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + wave;
+  if (blk >= total_blocks) return;
+  quant_qk_block<kD, kSmooth>(x, S, H, S_pad, nbp, blk, xmean, xq, xscale, lane);
+}
+
+// Partial per-channel amax of |V| over rows [chunk * chunk_rows, +chunk_rows)
+// of one (b, h), by a workgroup of 256 threads: with G = kD/8 channel groups,
+// thread t covers channels [8 (t%G), +8) of rows t/G + (256/G) i. `red` is
+// LDS of 256/G x kD floats. Every channel of the chunk is written (0 for an
+// empty chunk).
 template <int kD>
-__global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __restrict__ v, int S,
-                                                             int H, int nchunk, int chunk_rows,
-                                                             float* __restrict__ partial) {
+__device__ __forceinline__ void v_amax_chunk(const uint16_t* __restrict__ v, int S, int H, int nchunk,
+                                             int chunk_rows, int64_t bh, int chunk, float* __restrict__ partial,
+                                             float (*red)[kD]) {
   constexpr int kGroups = kD / 8, kRowSets = 256 / kGroups;
-  __shared__ float red[kRowSets][kD];
-  const int chunk = blockIdx.x;
-  const int64_t bh = blockIdx.y;
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
   const int cg = threadIdx.x % kGroups, ro = threadIdx.x / kGroups;
@@ -131,26 +138,61 @@ __global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __r
   }
 }
 
-// Quantize 128 keys x 128 channels of V to E4M3FN and write them transposed
-// ([channel][key]) with keys permuted inside each 64-key group.
-// grid (S_pad/128, B*H), 2 kD threads. Thread t covers channels
-// [8 (t/16), +8) of 8 keys that land in 8 consecutive slots: within a 32-key
-// block u of a 64-key group, key 32u + 4m + e (m = 0..7, e = 0..3) goes to
-// slot 32 (m%2) + 16u + 4 (m/2) + e, so quads m = g + 4pr and g + 4pr + 2
-// fill slots [32g + 16u + 8pr, +8). The 16 threads of a channel group write
-// one 128-byte row of the LDS tile between them.
+// grid B*H*nchunk, 256 threads: workgroup i takes chunk i % nchunk of (b, h)
+// = i / nchunk.
+template <int kD>
+__global__ __launch_bounds__(256) void v_amax_partial_kernel(const uint16_t* __restrict__ v, int S,
+                                                             int H, int nchunk, int chunk_rows,
+                                                             float* __restrict__ partial) {
+  __shared__ float red[256 / (kD / 8)][kD];
+  v_amax_chunk<kD>(v, S, H, nchunk, chunk_rows, blockIdx.x / nchunk, blockIdx.x % nchunk, partial, red);
+}
+
+// The K/V pre-pass in one launch: workgroups [0, nkwg) quantize K (four
+// 32-row blocks each, as quant_qk_kernel), the following B*H*nchunk
+// workgroups take V's per-chunk maxima (as v_amax_partial_kernel), so one
+// streaming pass reads both tensors.
+template <int kD>
+__global__ __launch_bounds__(256) void kv_prepass_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                         int S, int H, int S_pad, int nbp, int64_t total_blocks,
+                                                         int nkwg, int8_t* __restrict__ kq, float* __restrict__ ks,
+                                                         int nchunk, int chunk_rows, float* __restrict__ partial) {
+  __shared__ float red[256 / (kD / 8)][kD];
+  if ((int)blockIdx.x < nkwg) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + wave;
+    if (blk < total_blocks) quant_qk_block<kD, false>(k, S, H, S_pad, nbp, blk, nullptr, kq, ks, lane);
+  } else {
+    const int i = (int)blockIdx.x - nkwg;
+    v_amax_chunk<kD>(v, S, H, nchunk, chunk_rows, i / nchunk, i % nchunk, partial, red);
+  }
+}
+
+// Quantize V to E4M3FN and write it transposed ([channel][key]) with keys
+// permuted inside each 64-key group. grid B*H*nvt, 2 kD threads: workgroup
+// i takes up to kVTilesPerWg tiles of 128 keys, starting at key
+// 128 kVTilesPerWg (i % nvt), of (b, h) = i / nvt.
+// Per 128-key tile, thread t covers channels [8 (t/16), +8) of 8 keys that
+// land in 8 consecutive slots: within a 32-key block u of a 64-key group,
+// key 32u + 4m + e (m = 0..7, e = 0..3) goes to slot 32 (m%2) + 16u +
+// 4 (m/2) + e, so quads m = g + 4pr and g + 4pr + 2 fill slots [32g + 16u +
+// 8pr, +8). The 16 threads of a channel group write one 128-byte row of the
+// LDS tile between them.
 // Each workgroup first reduces the per-chunk maxima of its (b, h) to the
 // channel amax (at most 32 chunks) and forms scale = fl32(amax/448) and
 // inv = fl32(448/amax) (0 for amax = 0 or a non-finite reciprocal); the
-// workgroups of key tile 0 store the scales.
+// first workgroup of each (b, h) stores the scales.
+constexpr int kVTilesPerWg = 4;
+
 template <int kD>
 __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict__ v, int S, int H,
-                                                      int S_pad, const float* __restrict__ partial, int nchunk,
-                                                      float* __restrict__ vscale, uint8_t* __restrict__ vt) {
+                                                      int S_pad, int nvt, const float* __restrict__ partial,
+                                                      int nchunk, float* __restrict__ vscale,
+                                                      uint8_t* __restrict__ vt) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kD][128 + 16];
   __shared__ float red[2][kD];
-  const int k0 = blockIdx.x * 128;
-  const int64_t bh = blockIdx.y;
+  const int64_t bh = blockIdx.x / nvt;
+  const int vti = blockIdx.x % nvt;
   {
     const int c = threadIdx.x % kD, half = threadIdx.x / kD;
     float m = 0.0f;
@@ -166,7 +208,7 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
         if (!isfinite(inv)) { inv = 0.0f; scale = 0.0f; }
       }
       red[0][c] = inv;
-      if (blockIdx.x == 0) vscale[bh * kD + c] = scale;
+      if (vti == 0) vscale[bh * kD + c] = scale;
     }
     __syncthreads();
   }
@@ -179,59 +221,66 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict
   float inv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) inv[j] = red[0][cg * 8 + j];
-  float y[8][8];   // [key][channel]
+  for (int ti = 0; ti < kVTilesPerWg; ++ti) {
+    const int k0 = (vti * kVTilesPerWg + ti) * 128;
+    if (k0 >= S_pad) break;                       // uniform over the workgroup
+    float y[8][8];   // [key][channel]
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int row = k0 + kq0 + (e & 3) + 8 * (e >> 2);
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (row < S) w = *(const uint4*)(v + (((b * S + row) * H + h) * kD + cg * 8));
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    for (int e = 0; e < 8; ++e) {
+      const int row = k0 + kq0 + (e & 3) + 8 * (e >> 2);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (row < S) w = *(const uint4*)(v + (((b * S + row) * H + h) * kD + cg * 8));
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      y[e][2 * j] = fminf(fmaxf(bf16_to_f32(ws[j] & 0xFFFFu) * inv[2 * j], -448.0f), 448.0f);
-      y[e][2 * j + 1] = fminf(fmaxf(bf16_to_f32(ws[j] >> 16) * inv[2 * j + 1], -448.0f), 448.0f);
+      for (int j = 0; j < 4; ++j) {
+        y[e][2 * j] = fminf(fmaxf(bf16_to_f32(ws[j] & 0xFFFFu) * inv[2 * j], -448.0f), 448.0f);
+        y[e][2 * j + 1] = fminf(fmaxf(bf16_to_f32(ws[j] >> 16) * inv[2 * j + 1], -448.0f), 448.0f);
+      }
     }
-  }
+    if (ti > 0) __syncthreads();                  // the previous tile's copy-out has read `tile`
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0][j], y[1][j], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2][j], y[3][j], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4][j], y[5][j], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6][j], y[7][j], hi, true);
-    *(uint2*)(&tile[cg * 8 + j][slot]) = make_uint2((uint32_t)lo, (uint32_t)hi);
-  }
-  __syncthreads();
-  const int c = threadIdx.x >> 1, half = threadIdx.x & 1;
-  uint8_t* dst = vt + (bh * kD + c) * (int64_t)S_pad + k0 + 64 * half;
+    for (int j = 0; j < 8; ++j) {
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0][j], y[1][j], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2][j], y[3][j], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4][j], y[5][j], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6][j], y[7][j], hi, true);
+      *(uint2*)(&tile[cg * 8 + j][slot]) = make_uint2((uint32_t)lo, (uint32_t)hi);
+    }
+    __syncthreads();
+    const int c = threadIdx.x >> 1, half = threadIdx.x & 1;
+    uint8_t* dst = vt + (bh * kD + c) * (int64_t)S_pad + k0 + 64 * half;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *(uint4*)(dst + 16 * q) = *(const uint4*)(&tile[c][64 * half + 16 * q]);
+    for (int q = 0; q < 4; ++q)
+      *(uint4*)(dst + 16 * q) = *(const uint4*)(&tile[c][64 * half + 16 * q]);
+  }
 }
 
-// K smoothing, step 1: per (b, h, 32-row block) sum of each channel in
-// fp64 (rows >= S contribute nothing). bf16 values have 8 significant bits,
-// so these sums, and the sums of step 2, are exact in fp64 whenever the
-// values of a channel span fewer than 53 - 8 - log2(S) binades (for S =
-// 75600 and values of magnitude above 2^-20 times the channel's largest,
-// always).
-// With L = kD/8 lanes per block, 64/L blocks per wave: lane l covers
-// channels [8 (l%L), +8) of block (64/L) (4 blockIdx + wave) + l/L.
+// K smoothing, step 1: per (b, h, chunk of kKSumRows rows) sum of each
+// channel in fp64 (rows >= S contribute nothing). bf16 values have 8
+// significant bits, so these sums, and the sums of step 2, are exact in fp64
+// whenever the values of a channel span fewer than 53 - 8 - log2(S) binades
+// (for S = 75600 and values of magnitude above 2^-20 times the channel's
+// largest, always).
+// With L = kD/8 lanes per chunk, 64/L chunks per wave: lane l covers
+// channels [8 (l%L), +8) of chunk (64/L) (4 blockIdx + wave) + l/L.
+constexpr int kKSumRows = 256;
+
 template <int kD>
 __global__ __launch_bounds__(256) void k_block_sum_kernel(const uint16_t* __restrict__ k, int S, int H,
-                                                          int nbp, int64_t total_blocks,
+                                                          int nck, int64_t total_chunks,
                                                           double* __restrict__ partial) {
-  constexpr int kLanesPerBlock = kD / 8, kBlocksPerWave = 64 / kLanesPerBlock;
+  constexpr int kLanesPerChunk = kD / 8, kChunksPerWave = 64 / kLanesPerChunk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t blk = ((int64_t)blockIdx.x * 4 + wave) * kBlocksPerWave + lane / kLanesPerBlock;
-  if (blk >= total_blocks) return;
-  const int t = (int)(blk % nbp);
-  const int64_t bh = blk / nbp;
+  const int64_t ck = ((int64_t)blockIdx.x * 4 + wave) * kChunksPerWave + lane / kLanesPerChunk;
+  if (ck >= total_chunks) return;
+  const int t = (int)(ck % nck);
+  const int64_t bh = ck / nck;
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
-  const int col = (lane % kLanesPerBlock) * 8;
+  const int col = (lane % kLanesPerChunk) * 8;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int rend = min(S, (t + 1) * kQBlock);
-  for (int row = t * kQBlock; row < rend; ++row) {
+  const int rend = min(S, (t + 1) * kKSumRows);
+  for (int row = t * kKSumRows; row < rend; ++row) {
     const uint4 w = *(const uint4*)(k + (((b * S + row) * H + h) * kD + col));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -240,7 +289,7 @@ __global__ __launch_bounds__(256) void k_block_sum_kernel(const uint16_t* __rest
       acc[2 * j + 1] += (double)bf16_to_f32(ws[j] >> 16);
     }
   }
-  double2* dst = (double2*)(partial + blk * kD + col);
+  double2* dst = (double2*)(partial + ck * kD + col);
 #pragma unroll
   for (int j = 0; j < 4; ++j) dst[j] = make_double2(acc[2 * j], acc[2 * j + 1]);
 }
@@ -261,16 +310,16 @@ __device__ __forceinline__ float div_round_f32(double sum, double n) {
   return (up == ((double)nb > (double)f0)) ? nb : f0;
 }
 
-// K smoothing, step 2: the block sums added in fp64, then mean =
+// K smoothing, step 2: the chunk sums added in fp64, then mean =
 // fl32(sum / S) with one rounding. grid B*H, kD threads (one per channel).
 template <int kD>
-__global__ __launch_bounds__(128) void k_mean_kernel(const double* __restrict__ partial, int nbp, int S,
+__global__ __launch_bounds__(128) void k_mean_kernel(const double* __restrict__ partial, int nck, int S,
                                                      float* __restrict__ kmean) {
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
-  const double* p = partial + bh * (int64_t)nbp * kD + c;
+  const double* p = partial + bh * (int64_t)nck * kD + c;
   double sum = 0.0;
-  for (int t = 0; t < nbp; ++t) sum += p[(int64_t)t * kD];
+  for (int t = 0; t < nck; ++t) sum += p[(int64_t)t * kD];
   kmean[bh * kD + c] = div_round_f32(sum, (double)S);
 }
 

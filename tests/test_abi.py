@@ -52,16 +52,21 @@ def test_queries():
     assert bn % 32 == 0 and bn >= 32
     for S, Sp in ((1, 256), (256, 256), (257, 512), (75600, 75776), (16384, 16384)):
         assert sage.sage_seq_pad(S) == Sp
-    # workspace: three one-byte-per-element tensors plus small scales/scratch
+    # workspace: the one-byte K and V codes plus small scales/scratch (Q is
+    # quantized inside the attention kernel), i.e. about 2/3 byte per element
+    # of the three inputs
     for B, S, H in ((1, 256, 2), (1, 16384, 24), (2, 75600, 40)):
         Sp = sage.sage_seq_pad(S)
         ws = sage.sage_workspace_bytes(B, S, H, 128)
-        base = 3 * B * H * Sp * 128
+        base = 2 * B * H * Sp * 128
         assert base <= ws <= base * 1.02 + 65536
+        assert ws <= 0.68 * 3 * B * S * H * 128 + 65536
+        wx = sage.lib().sage_workspace_bytes_ex(B, S, S, H, 128)
+        assert base <= wx <= base * 1.03 + 65536
     assert sage.sage_workspace_bytes(1, 256, 2, 96) == 0
     # head dim 64: half the bytes of the one-byte tensors
     assert sage.sage_workspace_bytes(1, 256, 2, 64) < sage.sage_workspace_bytes(1, 256, 2, 128)
-    assert sage.sage_workspace_bytes(1, 256, 2, 64) >= 3 * 2 * 256 * 64
+    assert sage.sage_workspace_bytes(1, 256, 2, 64) >= 2 * 2 * 256 * 64
     assert sage.sage_workspace_bytes(0, 256, 2, 128) == 0
     assert sage.lib().sage_status_str(ERR_WS) == b"SAGE_ERR_WORKSPACE"
 
@@ -75,6 +80,13 @@ def test_validation_codes():
     p = ctypes.c_void_p
     f, m = p(FAKE), p(MISALIGNED)
     z = p(0)
+    # the fused K/V quantizer
+    assert _call("sage_quant_kv", f, f, 1, 256, 2, 96, f, f, f, f, f, 1 << 20, z) == ERR_UNSUP
+    assert _call("sage_quant_kv", f, z, 1, 256, 2, 128, f, f, f, f, f, 1 << 20, z) == ERR_NULL
+    assert _call("sage_quant_kv", f, f, 1, 256, 2, 128, f, f, f, m, f, 1 << 20, z) == ERR_ALIGN
+    assert _call("sage_quant_kv", f, f, 1, 256, 2, 128, f, f, f, f, f, 16, z) == ERR_WS
+    # B*H beyond 65535 is accepted by the size checks (1-D grids)
+    assert _call("sage_quant_kv", f, f, 1, 256, 70000, 128, f, f, f, f, f, 16, z) == ERR_WS
     # the allocation-free V quantizer: shapes beyond its static buffer
     assert _call("sage_quant_v_noalloc", f, 1, 16384, 513, 128, f, f, z) == ERR_WS
     assert b"static buffer" in sage.lib().sage_last_error()
@@ -116,15 +128,15 @@ def test_extended_entry_points_validation():
     for B, Sq, Skv, H in ((1, 300, 77, 2), (1, 64, 4096, 24), (2, 75600, 75600, 40)):
         ws = sage.sage_workspace_bytes_ex(B, Sq, Skv, H, 128)
         Sqp, Skp = sage.sage_seq_pad(Sq), sage.sage_seq_pad(Skv)
-        base = B * H * 128 * (Sqp + 2 * Skp)
-        assert base <= ws <= base * 1.15 + 65536   # + block sums of K smoothing (16 B per key row)
+        base = B * H * 128 * 2 * Skp               # K and V codes (Q is quantized in the kernel)
+        assert base <= ws <= base * 1.03 + 65536   # + scales and the larger scratch
         if Sq == Skv:
             assert ws >= sage.sage_workspace_bytes(B, Sq, H, 128)
     assert sage.sage_workspace_bytes_ex(1, 300, 0, 2, 128) == 0
     assert sage.sage_workspace_bytes_ex(1, 300, 77, 2, 96) == 0
     assert 0 < sage.sage_workspace_bytes_ex(1, 300, 77, 2, 64) < sage.sage_workspace_bytes_ex(1, 300, 77, 2, 128)
     nb = sage.sage_k_smooth_scratch_bytes(1, 300, 2, 128)
-    assert nb >= 2 * (sage.sage_seq_pad(300) // 32) * 128 * 4
+    assert nb >= 2 * 2 * 128 * 8                    # fp64 sums of two 256-row chunks per head
     # sage_quant_k_smooth
     assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, f, f, f, f, nb - 1, z) == ERR_WS
     assert _call("sage_quant_k_smooth", f, 1, 300, 2, 128, f, f, z, f, nb, z) == ERR_NULL

@@ -83,6 +83,40 @@ def test_quant_v_bit_exact(idx, S, H):
     assert np.all(tail == 0)
 
 
+@pytest.mark.parametrize("idx,S,H,D", [(2, 1000, 3, 128), (5, 333, 2, 128), (3, 4096, 2, 64), (1, 1, 1, 128)])
+def test_quant_kv_equals_separate_quantizers(idx, S, H, D):
+    _say(f"quant_kv config {idx} S={S} H={H} D={D}")
+    _, k, v = workloads.generate(idx, S=S, H=H, B=1, seed=250 + S)
+    k, v = np.ascontiguousarray(k[..., :D]), np.ascontiguousarray(v[..., :D])
+    kd, vd = to_dev(k), to_dev(v)
+    a = sage.sage_quant_kv(kd, vd)
+    k8, ks = sage.sage_quant_qk(kd)
+    v8, vs = sage.sage_quant_v(vd)
+    torch.cuda.synchronize()
+    for x, y in zip(a, (k8, ks, v8, vs)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    r8, rs = oracle.quant_qk(k)
+    assert np.array_equal(a[0].cpu().numpy()[:, :, :S], r8)
+    rv8, rvs = oracle.quant_v(v)
+    assert np.array_equal(unpermute_vt(a[2].cpu().numpy(), S), rv8)
+
+
+def test_quantizers_with_more_than_65535_heads():
+    """B*H above 65535 (the V kernels take B*H in grid.x)."""
+    B, S, H = 2, 3, 33000
+    _say(f"quantizers with B*H = {B * H}")
+    _, k, v = workloads.generate(1, S=S, H=H, B=B, seed=17)
+    kd, vd = to_dev(k), to_dev(v)
+    k8, ks, v8, vs = sage.sage_quant_kv(kd, vd)
+    torch.cuda.synchronize()
+    r8, rs = oracle.quant_qk(k)
+    assert np.array_equal(k8.cpu().numpy()[:, :, :S], r8)
+    assert np.array_equal(ks.cpu().numpy()[:, :, :1].view(np.uint32), rs.view(np.uint32))
+    rv8, rvs = oracle.quant_v(v)
+    assert np.array_equal(unpermute_vt(v8.cpu().numpy(), S), rv8)
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
+
+
 def test_quant_edge_values():
     _say("quant edge values")
     x = workloads.generate_custom((1, 96, 2, 128), seed=7)
