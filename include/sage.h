@@ -30,7 +30,7 @@
  *     each launch's grid (about B*H*S_pad/128 workgroups for the largest)
  *     must also stay below 2^31. Larger sizes return SAGE_ERR_SHAPE.
  *   - Head dim: D == 128 is the pages' operation. D == 64 is also accepted
- *     by every entry point except sage_debug_qk_scores (the pages' callers
+ *     by every entry point (the pages' callers
  *     fall back for it: the VAE's head dim 64, diffusers PR #15060, section
  *     "What does this PR do?"); every "128" channel count below then reads
  *     D. Other head dims return SAGE_ERR_UNSUPPORTED.
@@ -194,11 +194,14 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
 
 /*
  * sage_debug_qk_scores - debug dump of the exact int32 scores A = q8 . k8^T
- * of one (b, h), rows [r0, r0+nr) x keys [c0, c0+nc), computed by the same
- * INT8 MFMA operand loading and instruction sequence as sage_attn_fwd.
+ * of one (b, h), rows [r0, r0+nr) x keys [c0, c0+nc), computed through the
+ * attention kernel's own path: K tiles staged into LDS by the same
+ * buffer-to-LDS copies into the same swizzled layout, the same Q fragments,
+ * the same INT8 MFMA sequence with the accumulators starting from the bias
+ * 0x4B400000, which is subtracted when a score is stored.
  *   scores  int32 [nr, nc] out, row-major.
  * Windows must satisfy 0 <= r0, 0 < nr, r0+nr <= S_pad (same for keys).
- * D must be 128 (SAGE_ERR_UNSUPPORTED otherwise).
+ * D is 128 or 64.
  */
 sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t B, int64_t S,
                                  int64_t H, int64_t D, int64_t b, int64_t h, int64_t r0,

@@ -450,7 +450,6 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
                                  int64_t D, int64_t b, int64_t h, int64_t r0, int64_t nr, int64_t c0,
                                  int64_t nc, int32_t* scores, void* stream) {
   SAGE_TRY(check_shape(B, S, H, D));
-  if (D != 128) return fail(SAGE_ERR_UNSUPPORTED, "the score dump covers head dim 128 only");
   SAGE_TRY(check_ptr(q_i8, "q_i8"));
   SAGE_TRY(check_ptr(k_i8, "k_i8"));
   if (!scores) return fail(SAGE_ERR_NULL, "scores is NULL");
@@ -459,13 +458,21 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
   if (r0 < 0 || nr < 1 || r0 + nr > Sp || c0 < 0 || nc < 1 || c0 + nc > Sp)
     return fail(SAGE_ERR_RANGE, "window outside [0, S_pad)");
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
-  const int64_t rA = r0 / 32 * 32, cA = c0 / 128 * 128;
-  const int64_t gy = (r0 + nr - rA + sage::kDebugRows - 1) / sage::kDebugRows;
+  // query tiles of kQueryTile rows and key tiles of kKeyTile keys covering
+  // the window; S_pad is a multiple of both, so every staged row exists
+  const int64_t rA = r0 / sage::kQueryTile * sage::kQueryTile, cA = c0 / sage::kKeyTile * sage::kKeyTile;
+  const int64_t gy = (r0 + nr - rA + sage::kQueryTile - 1) / sage::kQueryTile;
   const int64_t gx = (c0 + nc - cA + sage::kKeyTile - 1) / sage::kKeyTile;
   if (gx > INT32_MAX || gy > 65535) return fail(SAGE_ERR_RANGE, "window too large");
-  hipLaunchKernelGGL(sage::debug_qk_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, (hipStream_t)stream,
-                     q_i8, k_i8, (int)Sp, b * H + h, (int)rA, (int)r0, (int)nr, (int)cA, (int)c0, (int)nc,
-                     scores);
+  hipStream_t st = (hipStream_t)stream;
+  if (D == 64)
+    hipLaunchKernelGGL(sage::debug_qk_kernel<64>, dim3((unsigned)gx, (unsigned)gy), dim3(64 * sage::kAttnWaves), 0,
+                       st, q_i8, k_i8, (int)Sp, b * H + h, (int)rA, (int)r0, (int)nr, (int)cA, (int)c0, (int)nc,
+                       scores);
+  else
+    hipLaunchKernelGGL(sage::debug_qk_kernel<128>, dim3((unsigned)gx, (unsigned)gy), dim3(64 * sage::kAttnWaves), 0,
+                       st, q_i8, k_i8, (int)Sp, b * H + h, (int)rA, (int)r0, (int)nr, (int)cA, (int)c0, (int)nc,
+                       scores);
   return launched("sage_debug_qk_scores");
 }
 

@@ -52,19 +52,6 @@ __device__ __forceinline__ int swz_key(int row) {
 template <int kRB>
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRB + ((chunk ^ swz_key<kRB>(row)) << 4); }
 
-// Cooperative copy of one 128-row x 128-byte tile (rows `row_stride` bytes
-// apart in global memory) into swizzled LDS. 256 threads, 4 x 16 B each.
-__device__ __forceinline__ void stage_tile(uint8_t* __restrict__ lds, const uint8_t* __restrict__ src,
-                                           int64_t row_stride, int tid) {
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = tid + 256 * it;
-    const int row = idx >> 3, ch = idx & 7;
-    const uint4 w = *(const uint4*)(src + row * row_stride + ch * 16);
-    *(uint4*)(lds + swz<128>(row, ch)) = w;
-  }
-}
-
 // The wave's Q fragment for head dim kD: lane l holds bytes
 // [kD/2 g, kD/2 g + kD/2) of query row l%32 (g = l/32, qrow points there);
 // step s of the kD-deep contraction uses 16 of them. K operands use the same
@@ -250,6 +237,60 @@ __device__ __forceinline__ void wait_tiles() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unchanged
 }
 
+// Staging of K and V^T tiles into LDS rings with buffer_load ... lds, for a
+// workgroup of kAttnWaves = 8 waves: lane l of a wave instruction writes LDS
+// bytes [16 l, 16 l + 16) of a 1 KB group of rows (K: 1024/kD rows of kD
+// bytes; V^T: 8 rows of 128 bytes), i.e. row grp * rows_per_group +
+// l / chunks_per_row and swizzled chunk l % chunks_per_row, so it reads the
+// source chunk XORed with the row's swizzle key. A tile is kD/8 groups, kD/64
+// per wave. The lane offsets are loop-invariant; the tile offset is a scalar.
+// Buffer descriptors cover one head's K rows and V^T rows (base, stride 0,
+// size in bytes < 2^31, default data format). `lds_k` and `lds_v` are slot 0
+// of rings whose slots are kKeyTile * kD bytes apart.
+template <int kD>
+struct KvStage {
+  static constexpr int kGroupsPerWave = kD / 64;
+  v4i rk, rv;
+  uint32_t koff[kGroupsPerWave], voff[kGroupsPerWave];
+  uint32_t kl0, vl0;
+
+  __device__ __forceinline__ KvStage(const uint8_t* kbase, const uint8_t* vbase, int Skv_pad, const uint8_t* lds_k,
+                                     const uint8_t* lds_v, int wave, int wave_s, int lane) {
+    const uint64_t kaddr = (uint64_t)(uintptr_t)kbase, vaddr = (uint64_t)(uintptr_t)vbase;
+    const uint32_t nbytes = (uint32_t)Skv_pad * kD;
+    rk = (v4i){__builtin_amdgcn_readfirstlane((int)(uint32_t)kaddr),
+               __builtin_amdgcn_readfirstlane((int)(uint32_t)(kaddr >> 32) & 0xFFFF),
+               __builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000};
+    rv = (v4i){__builtin_amdgcn_readfirstlane((int)(uint32_t)vaddr),
+               __builtin_amdgcn_readfirstlane((int)(uint32_t)(vaddr >> 32) & 0xFFFF),
+               __builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000};
+    constexpr int kKChunks = kD / 16;   // 16-byte chunks per K row
+#pragma unroll
+    for (int i = 0; i < kGroupsPerWave; ++i) {
+      const int grp = wave + 8 * i;
+      const int krow = (1024 / kD) * grp + lane / kKChunks;
+      koff[i] = (uint32_t)(krow * kD + (((lane % kKChunks) ^ swz_key<kD>(krow)) << 4));
+      const int vrow = 8 * grp + (lane >> 3);
+      voff[i] = (uint32_t)(vrow * Skv_pad + (((lane & 7) ^ swz_key<128>(vrow)) << 4));
+    }
+    // LDS byte address of the first 1 KB row group this wave writes per slot
+    kl0 = lds_addr(lds_k) + wave_s * 1024;
+    vl0 = lds_addr(lds_v) + wave_s * 1024;
+  }
+  // K tile t (keys [kKeyTile t, +kKeyTile)) into ring slot `slot`
+  __device__ __forceinline__ void load_k(int t, int slot) const {
+#pragma unroll
+    for (int i = 0; i < kGroupsPerWave; ++i)
+      dma16(rk, kl0 + slot * (kKeyTile * kD) + i * 8192, koff[i], (uint32_t)t * (kKeyTile * kD));
+  }
+  // V^T tile t (columns [kKeyTile t, +kKeyTile) of the kD rows) into slot
+  __device__ __forceinline__ void load_v(int t, int slot) const {
+#pragma unroll
+    for (int i = 0; i < kGroupsPerWave; ++i)
+      dma16(rv, vl0 + slot * (kD * kKeyTile) + i * 8192, voff[i], (uint32_t)t * kKeyTile);
+  }
+};
+
 struct RowState {
   float m, m2, l;
 };
@@ -368,46 +409,9 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   const float* ksb = kscale + bh * (Skv_pad / kQBlock);
   const int T = (Skv + kKeyTile - 1) / kKeyTile;
 
-  // Tiles stream into LDS with buffer_load ... lds: lane l of a wave
-  // instruction writes LDS bytes [16 l, 16 l + 16) of a 1 KB group of rows
-  // (K: 1024/kD rows of kD bytes; V^T: 8 rows of 128 bytes), i.e. row
-  // grp * rows_per_group + l / chunks_per_row and swizzled chunk
-  // l % chunks_per_row, so it reads the source chunk XORed with the row's
-  // swizzle key. A tile is kD/8 groups, kD/64 per wave. The lane offsets are
-  // loop-invariant; the tile offset is a scalar. Buffer descriptors cover
-  // this head's K rows and V^T rows (base, stride 0, size in bytes < 2^31,
-  // default data format).
-  const uint64_t kaddr = (uint64_t)(uintptr_t)kbase, vaddr = (uint64_t)(uintptr_t)vbase;
-  const uint32_t nbytes = (uint32_t)Skv_pad * kD;
-  const v4i rk = {__builtin_amdgcn_readfirstlane((int)(uint32_t)kaddr),
-                  __builtin_amdgcn_readfirstlane((int)(uint32_t)(kaddr >> 32) & 0xFFFF),
-                  __builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000};
-  const v4i rv = {__builtin_amdgcn_readfirstlane((int)(uint32_t)vaddr),
-                  __builtin_amdgcn_readfirstlane((int)(uint32_t)(vaddr >> 32) & 0xFFFF),
-                  __builtin_amdgcn_readfirstlane((int)nbytes), 0x00020000};
-  constexpr int kGroupsPerWave = kD / 64;
-  constexpr int kKChunks = kD / 16;   // 16-byte chunks per K row
-  uint32_t koff[kGroupsPerWave], voff[kGroupsPerWave];
-#pragma unroll
-  for (int i = 0; i < kGroupsPerWave; ++i) {
-    const int grp = wave + 8 * i;
-    const int krow = (1024 / kD) * grp + lane / kKChunks;
-    koff[i] = (uint32_t)(krow * kD + (((lane % kKChunks) ^ swz_key<kD>(krow)) << 4));
-    const int vrow = 8 * grp + (lane >> 3);
-    voff[i] = (uint32_t)(vrow * Skv_pad + (((lane & 7) ^ swz_key<128>(vrow)) << 4));
-  }
-  // LDS byte address of the first 1 KB row group this wave writes per slot.
-  const uint32_t kl0 = lds_addr(lds_k[0]) + wave_s * 1024, vl0 = lds_addr(lds_v[0]) + wave_s * 1024;
-  auto load_k = [&](int t, int slot) {
-#pragma unroll
-    for (int i = 0; i < kGroupsPerWave; ++i)
-      dma16(rk, kl0 + slot * (kKeyTile * kD) + i * 8192, koff[i], (uint32_t)t * (kKeyTile * kD));
-  };
-  auto load_v = [&](int t, int slot) {
-#pragma unroll
-    for (int i = 0; i < kGroupsPerWave; ++i)
-      dma16(rv, vl0 + slot * (kD * kKeyTile) + i * 8192, voff[i], (uint32_t)t * kKeyTile);
-  };
+  const KvStage<kD> stage(kbase, vbase, Skv_pad, lds_k[0], lds_v[0], wave, wave_s, lane);
+  auto load_k = [&](int t, int slot) { stage.load_k(t, slot); };
+  auto load_v = [&](int t, int slot) { stage.load_v(t, slot); };
 
   load_k(0, 0);
   load_v(0, 0);
@@ -538,33 +542,44 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   }
 }
 
-// Debug dump of int32 scores through the same staging and MFMA path.
-// grid (key tiles, query tiles of kDebugRows = 128), 256 threads.
-__global__ __launch_bounds__(256) void debug_qk_kernel(const int8_t* __restrict__ q8,
-                                                       const int8_t* __restrict__ k8, int S_pad,
-                                                       int64_t bh, int rA, int r0, int nr, int cA,
-                                                       int c0, int nc, int32_t* __restrict__ scores) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kKeyTile * 128];
+// Debug dump of the int32 scores of one (b, h) through the attention
+// kernel's own path: K tiles staged into LDS by KvStage (buffer-to-LDS
+// copies into the swizzled slot), the wave's Q fragment in VGPRs, the INT8
+// MFMA sequence of qk_tile with accumulators starting from the bias
+// 0x4B400000; the bias is subtracted when a score is stored.
+// grid (key tiles of the window, query tiles of kQueryTile rows), 8 waves.
+template <int kD>
+__global__ __launch_bounds__(64 * kAttnWaves) void debug_qk_kernel(const int8_t* __restrict__ q8,
+                                                                  const int8_t* __restrict__ k8, int S_pad,
+                                                                  int64_t bh, int rA, int r0, int nr, int cA,
+                                                                  int c0, int nc, int32_t* __restrict__ scores) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[kKeyTile * kD];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int k0 = cA + blockIdx.x * kKeyTile;
-  const int qa = rA + blockIdx.y * kDebugRows + wave * 32;
-  stage_tile(lds_k, (const uint8_t*)k8 + (bh * S_pad + k0) * kHeadDim, kHeadDim, tid);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int t = cA / kKeyTile + blockIdx.x;
+  const uint8_t* kbase = (const uint8_t*)k8 + bh * S_pad * kD;
+  const KvStage<kD> stage(kbase, kbase, S_pad, lds_k, lds_k, wave, wave_s, lane);
+  stage.load_k(t, 0);
+  wait_tiles();
   __syncthreads();
-  if (qa >= S_pad) return;
-  v4i qf[4];
-  load_q_frag<kHeadDim>(q8 + ((bh * S_pad + qa + li) * kHeadDim + 64 * g), qf);
+  const int qa = rA + blockIdx.y * kQueryTile + wave * 32;
+  v4i qf[kD / 32];
+  load_q_frag<kD>(q8 + ((bh * S_pad + qa + li) * kD + (kD / 2) * g), qf);
+  v16i bias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bias[r] = kScoreBias;
   v16i sacc[4];
-  const v16i zero = {0};
-  qk_tile<kHeadDim>(lds_k, qf, li, g, zero, sacc);
+  qk_tile<kD>(lds_k, qf, li, g, bias, sacc);
   const int row = qa + li;
   if (row < r0 || row >= r0 + nr) return;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = k0 + key_of(u, r, g);
-      if (key >= c0 && key < c0 + nc) scores[(int64_t)(row - r0) * nc + (key - c0)] = sacc[u][r];
+      const int key = t * kKeyTile + key_of(u, r, g);
+      if (key >= c0 && key < c0 + nc)
+        scores[(int64_t)(row - r0) * nc + (key - c0)] = sacc[u][r] - kScoreBias;
     }
 }
 

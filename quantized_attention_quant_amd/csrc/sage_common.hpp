@@ -12,7 +12,6 @@ constexpr int kSeqAlign = 256;    // padding of the quantized layouts
 constexpr int kKeyTile = 128;     // BN: keys per online-softmax tile
 constexpr int kAttnWaves = 8;     // waves per attention workgroup
 constexpr int kQueryTile = 32 * kAttnWaves;     // BM: queries per workgroup
-constexpr int kDebugRows = 128;                 // query rows per debug-dump workgroup
 constexpr int kVGroup = 64;       // keys per permuted group of the V^T layout
 constexpr int kVChunkRows = 512;  // minimum rows per partial-amax chunk of V
 

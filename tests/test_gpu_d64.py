@@ -112,3 +112,18 @@ def test_attention_d64_large_sampled():
         p = np.exp(s)
         ex = (p @ v[0, :, h, :].astype(np.float64)) / p.sum(axis=1, keepdims=True)
         gate(g, ref, ex, f"head {h} rows={len(rows)}")
+
+
+def test_debug_scores_d64():
+    _say("debug scores D=64")
+    q, k, _ = workloads.generate(2, S=700, H=2, B=1, seed=55)
+    q, k = d64(q), d64(k)
+    q8, _ = sage.sage_quant_qk(to_dev(q))
+    k8, _ = sage.sage_quant_qk(to_dev(k))
+    oq, _ = oracle.quant_qk(q)
+    ok, _ = oracle.quant_qk(k)
+    for (r0, nr, c0, nc) in [(0, 700, 0, 700), (250, 33, 600, 100)]:
+        got = sage.sage_debug_qk_scores(q8, k8, 1, 700, 2, 0, 1, r0, nr, c0, nc, D=D)
+        torch.cuda.synchronize()
+        ref = oracle.qk_scores(oq[0, 1], ok[0, 1])[r0:r0 + nr, c0:c0 + nc]
+        assert np.array_equal(got.cpu().numpy(), ref)
