@@ -96,7 +96,7 @@ def test_validation_codes():
     assert _call("sage_quant_qk", f, 1, 256, 2, 256, f, f, z) == ERR_UNSUP
     assert _call("sage_quant_qk", f, 0, 256, 2, 128, f, f, z) == ERR_SHAPE
     # the score dump covers head dim 128 only
-    assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 64, 0, 0, 0, 1, 0, 1, f, z) == ERR_UNSUP
+    assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 96, 0, 0, 0, 1, 0, 1, f, z) == ERR_UNSUP
     assert _call("sage_quant_qk", f, 1, -5, 2, 128, f, f, z) == ERR_SHAPE
     assert _call("sage_quant_qk", f, 1, 1 << 40, 2, 128, f, f, z) == ERR_SHAPE
     assert _call("sage_quant_qk", f, 1, (1 << 24) + 1, 2, 128, f, f, z) == ERR_SHAPE
