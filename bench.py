@@ -3,21 +3,23 @@
 A step is one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: INT8 quantization of K and FP8 quantization of V
 (sage_quant_kv: one pass over K and V, then V's quantization), and the fused
-attention kernel, which quantizes Q to INT8 itself (each wave's 32
-queries are one quantization block; the codes equal sage_quant_qk's). The workload is the image-DiT 2048^2 shape,
-B=1 S=16384 H=24 D=128, bf16, with the seeded outlier recipe of the
-``workloads`` module (config 3).
+attention kernel, which quantizes Q to INT8 itself (each wave's 32 queries
+are one quantization block; the codes equal sage_quant_qk's). The default
+workload is the image-DiT 2048^2 shape, B=1 S=16384 H=24 D=128, bf16, with
+the seeded outlier recipe of the ``workloads`` module (config 3); ``--config
+N`` times workload N (1-5) instead, one JSON line per run.
 
 Output: one JSON line. ``value`` is the effective throughput of the whole
 step, 4*B*H*S^2*D / (time per step), in TOPS. The ``roofline`` object covers
 the dominant kernel (the attention kernel, entry point sage_attn_fwd_qbf16):
-its launches are bracketed by HIP events
-on the stream they run on, inside the timed region. ``valu_issue`` puts the
-same launches against the vector-ALU issue rate, the limit the softmax
-arithmetic sets (instruction counts from the committed counter summary).
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+its launches are bracketed by HIP events on the stream they run on, inside
+the timed region. ``valu_issue`` puts the same launches against the
+vector-ALU issue rate (instruction counts from the committed counter summary
+of the default workload). ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload, in a pool of worker processes (one thread each)
+started before the GPU is touched.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -38,6 +40,13 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # wave64 VALU issue: 256 CUs x 4 SIMDs, one instruction per SIMD per 4 cycles at 2.4 GHz
 VALU_ISSUE_PEAK_G = 1024 * 2.4e9 / 4 / 1e9
 CONFIG_INDEX = 3
+WORKLOAD_NAMES = {
+    1: "tiny attention: B=1 S=256 H=2 D=128 bf16, N(0,1)",
+    2: "image-DiT 1024^2 attention: B=1 S=4096 H=24 D=128 bf16, K channel offsets",
+    3: "image-DiT 2048^2 attention: B=1 S=16384 H=24 D=128 bf16, outlier recipe",
+    4: "video-DiT attention: B=1 S=30720 H=24 D=128 bf16, K channel offsets",
+    5: "720p video-DiT attention: B=2 S=75600 H=40 D=128 bf16, K offsets on all channels",
+}
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_image_dit_2048_traffic.txt")
 VALU_PROFILE = os.path.join(ROOT, "profiles", "attn_fwd_image_dit_2048_valu.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_quant_amd", "csrc", n)
@@ -90,47 +99,76 @@ def valu_issue(attn_ms):
             "frac": round(achieved / VALU_ISSUE_PEAK_G, 4), "slots_per_launch": slots}
 
 
-def cpu_baseline(q, k, v, scale, bn, budget_s=15.0):
-    """Time the oracle on a bounded sample: one head, quantization of its
-    full K/V, then query blocks until about ``budget_s`` seconds."""
+_POOL_INPUTS = None   # (q, k, v, scale, bn), inherited by forked workers
+
+
+def _oracle_rows_worker(task):
+    """One worker of the CPU baseline: the oracle's quantization of one head
+    and its attention for query rows in chunks, until the deadline."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    S, D = q.shape[1], q.shape[3]
-    sl = lambda x: np.ascontiguousarray(x[0:1, :, 0:1, :])  # noqa: E731
+    b, h, deadline, chunk = task
+    q, k, v, scale, bn = _POOL_INPUTS
+    S = q.shape[1]
     t0 = time.perf_counter()
+    sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1, :])  # noqa: E731
     q8, qs = oracle.quant_qk(sl(q))
     k8, ks = oracle.quant_qk(sl(k))
     v8, vs = oracle.quant_v(sl(v))
     t_quant = time.perf_counter() - t0
-    rows_done = 0
-    t_attn = 0.0
-    chunk = 256
-    while t_attn < budget_s and rows_done < S:
-        rows = np.arange(rows_done, min(S, rows_done + chunk))
-        t1 = time.perf_counter()
-        oracle.attention_head(q8[0, 0], qs[0, 0], k8[0, 0], ks[0, 0], v8[0, 0], vs[0, 0], scale, bn, rows=rows)
-        t_attn += time.perf_counter() - t1
-        rows_done += len(rows)
-    # per-row cost of attention plus the per-head quantization, scaled to the
-    # whole workload's rows and heads
-    ops = 4.0 * rows_done * S * D
-    tops = ops / (t_attn + t_quant * rows_done / S) / 1e12
+    rows = 0
+    while rows < S and time.perf_counter() < deadline:
+        r = np.arange(rows, min(S, rows + chunk))
+        oracle.attention_head(q8[0, 0], qs[0, 0], k8[0, 0], ks[0, 0], v8[0, 0], vs[0, 0], scale, bn, rows=r)
+        rows += len(r)
+    return rows, t_quant, time.perf_counter() - t0
+
+
+def cpu_baseline(q, k, v, scale, bn, budget_s=15.0, workers=None):
+    """Time the oracle on a bounded sample: a pool of single-threaded worker
+    processes (fork, before any GPU use), one (b, h) head each, quantizing
+    the head's full Q/K/V and then attending query rows in chunks of 256
+    against all keys until ``budget_s`` seconds have passed. Effective ops
+    4*rows*S*D over the pool's wall time."""
+    import multiprocessing as mp
+
+    global _POOL_INPUTS
+    B, S, H, D = q.shape
+    ncpu = os.cpu_count() or 1
+    workers = workers or max(1, min(16, ncpu, B * H))
+    heads = [(b, h) for b in range(B) for h in range(H)][:workers]
+    _POOL_INPUTS = (q, k, v, scale, bn)
+    t0 = time.perf_counter()
+    deadline = t0 + budget_s
+    ctx = mp.get_context("fork")
+    with ctx.Pool(len(heads), initializer=_single_thread) as pool:
+        res = pool.map(_oracle_rows_worker, [(b, h, deadline, 256) for b, h in heads])
+    wall = time.perf_counter() - t0
+    _POOL_INPUTS = None
+    rows = sum(r[0] for r in res)
+    tq = max(r[1] for r in res)
+    tops = 4.0 * rows * S * D / wall / 1e12
     return {
         "value": tops,
         "unit": "TOPS",
-        "cores": threads,
+        "cores": len(heads),
         "kind": "oracle",
-        "sample": (f"head (b=0,h=0): quantization of its full Q/K/V ({t_quant:.1f} s) plus "
-                   f"{rows_done} of {S} query rows against all {S} keys ({t_attn:.1f} s); "
-                   f"effective ops 4*rows*S*D over the time, quantization prorated by rows; "
-                   f"numpy elementwise work is single-threaded, BLAS used {threads} threads"),
+        "sample": (f"{len(heads)} worker processes (os.cpu_count() = {ncpu}), one thread each, one (b, h) head "
+                   f"each: quantization of the head's full Q/K/V (up to {tq:.1f} s), then {rows} query rows in "
+                   f"all against all {S} keys, within {wall:.1f} s of wall time; effective ops 4*rows*S*D "
+                   f"over the wall time"),
     }
+
+
+def _single_thread():
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
 
 
 def main():
@@ -138,6 +176,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=CONFIG_INDEX, choices=[1, 2, 3, 4, 5],
+                    help="workload (default 3, the image-DiT 2048^2 shape the metric is quoted on)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -166,11 +206,13 @@ def main():
     import quantized_attention_quant_amd as sage
     import workloads
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = workloads.config(CONFIG_INDEX)
+    cfg = workloads.config(args.config)
     B, S, H, D = cfg.B, cfg.S, cfg.H, cfg.D
     scale = cfg.softmax_scale
-    q, k, v = workloads.generate(CONFIG_INDEX)
+    q, k, v = workloads.generate(args.config, chunk_elems=1 << 26)
+    # the CPU baseline first: its worker processes are forked before any GPU use
+    cpu = None if args.no_cpu_baseline else cpu_baseline(q, k, v, scale, 128, args.cpu_budget)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     to = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)  # noqa: E731
     qd, kd, vd = to(q), to(k), to(v)
@@ -219,7 +261,9 @@ def main():
     value = ops / (ms_per_step * 1e-3) / 1e12
     attn_avg = float(np.mean(attn_ms))
     achieved = ops / (attn_avg * 1e-3) / 1e12
-    traffic = measured_traffic()
+    # the counter summaries were taken on the default workload
+    headline = args.config == CONFIG_INDEX
+    traffic = measured_traffic() if headline else None
     # K: read 2N, write N; V: read 2N for its amax, read 2N again and write N
     pre_bytes = 8.0 * cfg.numel
     pre_avg = float(np.mean(pre_ms))
@@ -236,8 +280,8 @@ def main():
         "vs_baseline": None,
         "dtype": "int8+fp8e4m3 (int32/fp32 accumulate, fp32 softmax)",
         "data": "synthetic (seeded recipe, no trained weights)",
-        "config": {"workload": "image-DiT 2048^2 attention: B=1 S=16384 H=24 D=128 bf16, outlier recipe",
-                   "B": B, "S": S, "H": H, "D": D, "softmax_scale": scale},
+        "config": {"workload": WORKLOAD_NAMES[args.config], "B": B, "S": S, "H": H, "D": D,
+                   "softmax_scale": scale},
         "attn_fwd_ms": {"mean": round(attn_avg, 4), "median": round(float(np.median(attn_ms)), 4),
                         "min": round(min(attn_ms), 4), "max": round(max(attn_ms), 4),
                         "first_call": cold_ms},
@@ -253,10 +297,10 @@ def main():
             "frac": round(achieved / MFMA_PEAK_TOPS, 4),
             "traffic": traffic,
         },
-        "valu_issue": valu_issue(attn_avg),
+        "valu_issue": valu_issue(attn_avg) if headline else None,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(q, k, v, scale, sage.sage_kv_tile(), args.cpu_budget)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -208,6 +208,24 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
                                  int64_t nr, int64_t c0, int64_t nc, int32_t* scores,
                                  void* stream);
 
+/*
+ * sage_debug_p_codes - debug run of sage_attn_fwd that also stores the FP8
+ * E4M3FN codes of P' = 448 * 2^(t - m) as the attention kernel forms them:
+ * per key tile of sage_kv_tile() keys, against the running row maximum m
+ * after that tile (the online softmax of diffusers issue #15014, "gfx1201
+ * (RDNA4) SageAttention attention backend: aiter package or Hub kernel?",
+ * problem statement: FP32 softmax, FP8 PV with the fixed scale 448).
+ *   q_i8 .. v_scale, B, S, H, D, softmax_scale, out  as sage_attn_fwd (out
+ *            receives the same output bit for bit).
+ *   codes    uint8 [B, H, S, S_pad] out, caller-owned: codes[b,h,i,j] is the
+ *            code of query i and key j (natural key order); keys >= S are 0.
+ * S <= 16384 (SAGE_ERR_RANGE otherwise). Test and diagnostic use only.
+ */
+sage_status sage_debug_p_codes(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
+                               const float* k_scale, const uint8_t* v_fp8_t, const float* v_scale,
+                               int64_t B, int64_t S, int64_t H, int64_t D, float softmax_scale,
+                               uint8_t* codes, void* out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Extensions beyond the gfx1201 operation: log-sum-exp output, query and
  * key/value sequences of different lengths, and optional K smoothing.

@@ -21,7 +21,7 @@ __all__ = [
     "sage_attn_fwd", "sage_attention", "sage_debug_qk_scores", "v_key_order",
     "SAGE_SMOOTH_K", "sage_k_smooth_scratch_bytes", "sage_quant_k_smooth", "sage_attn_fwd_ex",
     "sage_workspace_bytes_ex", "sage_attention_ex", "sage_attn_fwd_qbf16", "sage_quant_v_noalloc",
-    "sage_quant_kv",
+    "sage_quant_kv", "sage_debug_p_codes",
 ]
 
 SAGE_SMOOTH_K = 1
@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
         "sage_attention": (ctypes.c_int, [p, p, p, i64, i64, i64, i64, f32, p, p, sz, p]),
         "sage_debug_qk_scores": (ctypes.c_int, [p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                                 i64, p, p]),
+        "sage_debug_p_codes": (ctypes.c_int, [p, p, p, p, p, p, i64, i64, i64, i64, f32, p, p, p]),
         "sage_k_smooth_scratch_bytes": (sz, [i64, i64, i64, i64]),
         "sage_quant_k_smooth": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p, p, sz, p]),
         "sage_attn_fwd_ex": (ctypes.c_int, [p, p, p, p, p, p, i64, i64, i64, i64, i64, f32, p, p, p]),
@@ -296,6 +297,28 @@ def sage_debug_qk_scores(q_i8, k_i8, B, S, H, b, h, r0, nr, c0, nc, D=128, score
     _check(lib().sage_debug_qk_scores(_ptr(q_i8), _ptr(k_i8), B, S, H, D, b, h, r0, nr, c0, nc,
                                       _ptr(scores), _stream_ptr(stream)))
     return scores
+
+
+def sage_debug_p_codes(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, H, D=128, softmax_scale=None,
+                       codes=None, out=None, stream=None):
+    """Attention (as sage_attn_fwd) that also returns the FP8 codes of P per
+    (b, h, query, key): uint8 [B, H, S, S_pad]. Returns (out, codes)."""
+    torch = _torch()
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    dev = q_i8.device
+    Sp = sage_seq_pad(S)
+    if codes is None:
+        codes = torch.zeros((B, H, S, Sp), dtype=torch.uint8, device=dev)
+    _require(codes, torch.uint8, "codes")
+    if codes.numel() < B * H * S * Sp:
+        raise ValueError("codes buffer too small")
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
+    _check(lib().sage_debug_p_codes(_ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(v_fp8_t),
+                                    _ptr(v_scale), B, S, H, D, float(softmax_scale), _ptr(codes), _ptr(out),
+                                    _stream_ptr(stream)))
+    return out, codes
 
 
 def sage_k_smooth_scratch_bytes(B, S, H, D=128) -> int:

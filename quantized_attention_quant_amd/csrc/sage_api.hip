@@ -24,6 +24,7 @@ static __device__ __align__(256) uint8_t scratch[SAGE_NOALLOC_SCRATCH_BYTES];
 namespace {
 
 constexpr int kAbiVersion = 1;
+constexpr int64_t kDebugPMaxSeq = 16384;  // sage_debug_p_codes: S x S_pad bytes per head
 thread_local char g_last_error[512] = "";
 
 sage_status fail(sage_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -256,13 +257,13 @@ sage_status quant_kv_impl(const void* k, const void* v, int64_t B, int64_t S, in
   return launched("sage_quant_kv");
 }
 
-template <int kD, bool kQuantQ>
+template <int kD, bool kQuantQ, bool kDump = false>
 void launch_attn(const int8_t* q8, const float* qs, const void* qraw, const int8_t* k8, const float* ks,
                  const uint8_t* vt, const float* vs, int64_t Sq, int64_t Skv, int64_t H, int nqt, int64_t nwg,
-                 float c, float log2_448, void* out, float* lse, hipStream_t st) {
-  hipLaunchKernelGGL((sage::attn_fwd_kernel<kD, kQuantQ>), dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0, st,
-                     q8, qs, (const uint16_t*)qraw, k8, ks, vt, vs, (int)Sq, (int)Skv, (int)H, (int)seq_pad(Sq),
-                     (int)seq_pad(Skv), nqt, (int)nwg, c, log2_448, (uint16_t*)out, lse);
+                 float c, float log2_448, void* out, float* lse, hipStream_t st, uint8_t* pdump = nullptr) {
+  hipLaunchKernelGGL((sage::attn_fwd_kernel<kD, kQuantQ, kDump>), dim3((unsigned)nwg), dim3(64 * sage::kAttnWaves), 0,
+                     st, q8, qs, (const uint16_t*)qraw, k8, ks, vt, vs, (int)Sq, (int)Skv, (int)H, (int)seq_pad(Sq),
+                     (int)seq_pad(Skv), nqt, (int)nwg, c, log2_448, (uint16_t*)out, lse, pdump);
 }
 
 // Fused attention. Q comes either quantized (q8, qs) or, when qraw is not
@@ -416,6 +417,38 @@ sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
   return attn_impl(q_i8, q_scale, nullptr, k_i8, k_scale, v_fp8_t, v_scale, B, S, S, H, D, softmax_scale, out,
                    nullptr, (hipStream_t)stream);
+}
+
+sage_status sage_debug_p_codes(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                               const uint8_t* v_fp8_t, const float* v_scale, int64_t B, int64_t S, int64_t H,
+                               int64_t D, float softmax_scale, uint8_t* codes, void* out, void* stream) {
+  SAGE_TRY(check_shape(B, S, H, D));
+  SAGE_TRY(check_ptr(q_i8, "q_i8"));
+  SAGE_TRY(check_ptr(q_scale, "q_scale"));
+  SAGE_TRY(check_ptr(k_i8, "k_i8"));
+  SAGE_TRY(check_ptr(k_scale, "k_scale"));
+  SAGE_TRY(check_ptr(v_fp8_t, "v_fp8_t"));
+  SAGE_TRY(check_ptr(v_scale, "v_scale"));
+  SAGE_TRY(check_ptr(out, "out"));
+  if (!codes) return fail(SAGE_ERR_NULL, "codes is NULL");
+  if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
+    return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite and >= 0");
+  if (S > kDebugPMaxSeq) return fail(SAGE_ERR_RANGE, "S above %d (the code dump is S x S_pad bytes per head)",
+                                     kDebugPMaxSeq);
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  const int nqt = (int)((S + sage::kQueryTile - 1) / sage::kQueryTile);
+  const int64_t nwg = B * H * nqt;
+  if (nwg > INT32_MAX) return fail(SAGE_ERR_SHAPE, "grid too large");
+  const float c = softmax_scale * (float)1.4426950408889634;
+  const float log2_448 = (float)std::log2(448.0);
+  hipStream_t st = (hipStream_t)stream;
+  if (D == 64)
+    launch_attn<64, false, true>(q_i8, q_scale, nullptr, k_i8, k_scale, v_fp8_t, v_scale, S, S, H, nqt, nwg, c,
+                                 log2_448, out, nullptr, st, codes);
+  else
+    launch_attn<128, false, true>(q_i8, q_scale, nullptr, k_i8, k_scale, v_fp8_t, v_scale, S, S, H, nqt, nwg, c,
+                                  log2_448, out, nullptr, st, codes);
+  return launched("sage_debug_p_codes");
 }
 
 sage_status sage_attention(const void* q, const void* k, const void* v, int64_t B, int64_t S, int64_t H,

@@ -173,10 +173,11 @@ constexpr float kScoreBiasF = 12582912.0f;     // 1.5 * 2^23
 // exponent is then one fused multiply-add, i.e. the exact A f - m2 rounded
 // once.
 // kClamp: saturate before the conversion (the hardware conversion gives NaN
-// above 464). kTail: keys at or past `nvalid` get P' = 0.
-template <bool kClamp, bool kTail>
+// above 464). kTail: keys at or past `nvalid` get P' = 0. kDump: also store
+// the codes to prow[key] (key within the tile; debug builds of the kernel).
+template <bool kClamp, bool kTail, bool kDump = false>
 __device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], float m2, int nvalid, int g,
-                                           v8i pop[2]) {
+                                           v8i pop[2], uint8_t* prow = nullptr) {
   // eight independent partial sums keep the additions off the critical path
   float ls[8];
 #pragma unroll
@@ -199,6 +200,8 @@ __device__ __forceinline__ float softmax_p(const v16i s[4], const float f[4], fl
       int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
       wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
       pop[u >> 1][4 * (u & 1) + j] = wd;
+      // the four codes are keys 32 u + 8 j + 4 g + (0..3): one 4-byte store
+      if (kDump && prow != nullptr) *(uint32_t*)(prow + 32 * u + 8 * j + 4 * g) = (uint32_t)wd;
     }
   }
   return ((ls[0] + ls[1]) + (ls[2] + ls[3])) + ((ls[4] + ls[5]) + (ls[6] + ls[7]));
@@ -298,10 +301,10 @@ struct RowState {
 // Vector phase of one key tile for one wave: running max, rescale of l and
 // O, P' and its FP8 codes. ks4 holds the scales of the tile's four 32-key
 // K blocks.
-template <int kD, bool kTail>
+template <int kD, bool kTail, bool kDump = false>
 __device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const float4 ks4, float c,
                                              float log2_448, int nvalid, int g, RowState& st, v16f o[kD / 32],
-                                             v8i pop[2]) {
+                                             v8i pop[2], uint8_t* prow = nullptr) {
   float f[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) f[u] = (qs * (u == 0 ? ks4.x : u == 1 ? ks4.y : u == 2 ? ks4.z : ks4.w)) * c;
@@ -337,9 +340,9 @@ __device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const fl
   // < 464, the limit of the conversion (above it the hardware gives NaN).
   // Larger maxima (outlier-scale Q/K blocks) take the saturating variant.
   if (__builtin_expect(__ballot(fabsf(m_new) >= 131072.0f) != 0, 0))
-    lsum = softmax_p<true, kTail>(s, f, m2_new, nvalid, g, pop);
+    lsum = softmax_p<true, kTail, kDump>(s, f, m2_new, nvalid, g, pop, prow);
   else
-    lsum = softmax_p<false, kTail>(s, f, m2_new, nvalid, g, pop);
+    lsum = softmax_p<false, kTail, kDump>(s, f, m2_new, nvalid, g, pop, prow);
   st.l = st.l * alpha + lsum;
   if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
@@ -381,14 +384,16 @@ __device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int
 // wave's vector work fills the cycles between them. Interval i reads K tiles i, i+1 and V tiles i-1, i,
 // and loads K tile i+2 and V tile i+1 into the third slot of each
 // three-stage LDS ring.
-template <int kD, bool kQuantQ>
+// kDump (debug instantiation): the P codes of every tile are also stored to
+// pdump [B, H, Sq, Skv_pad] (key order; padded keys 0).
+template <int kD, bool kQuantQ, bool kDump = false>
 __global__ __launch_bounds__(64 * kAttnWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qscale,
                      const uint16_t* __restrict__ qraw,
                      const int8_t* __restrict__ k8, const float* __restrict__ kscale,
                      const uint8_t* __restrict__ v8t, const float* __restrict__ vscale, int Sq, int Skv,
                      int H, int Sq_pad, int Skv_pad, int nqt, int num_wg, float c, float log2_448,
-                     uint16_t* __restrict__ out, float* __restrict__ lse) {
+                     uint16_t* __restrict__ out, float* __restrict__ lse, uint8_t* __restrict__ pdump) {
   static_assert(kAttnWaves == 8, "the phase skew pairs waves w and w + 4");
   static_assert(kD == 128 || kD == 64, "head dims 64 and 128");
   // K tile: kKeyTile rows of kD bytes; V^T tile: kD rows of kKeyTile bytes
@@ -403,6 +408,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const bool lead = wave_s < 4;
   const int q0 = qt * kQueryTile + wave * 32;
+  uint8_t* prow = (kDump && q0 + li < Sq) ? pdump + ((bh * Sq + q0 + li) * (int64_t)Skv_pad) : nullptr;
+  auto prow_at = [&](int i) { return prow != nullptr ? prow + i * kKeyTile : nullptr; };
 
   const uint8_t* kbase = (const uint8_t*)k8 + bh * Skv_pad * kD;
   const uint8_t* vbase = v8t + bh * kD * (int64_t)Skv_pad;
@@ -460,7 +467,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
       if (i + 2 < T) load_k(i + 2, (sl + 2) % 3);
       load_v(i + 1, (sl + 1) % 3);
       const float4 ksn = *(const float4*)(ksb + (i + 1) * (kKeyTile / kQBlock));
-      vector_phase<kD, false>(s, qs, ksc, c, log2_448, kKeyTile, g, st, o, pop);
+      vector_phase<kD, false, kDump>(s, qs, ksc, c, log2_448, kKeyTile, g, st, o, pop, prow_at(i));
       ksc = ksn;
       __builtin_amdgcn_s_setprio(2);
       qk_tile<kD>(lds_k[(sl + 1) % 3], qf, li, g, bias, s);
@@ -478,7 +485,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
     if (i0 < T - 1) step(i0++, std::integral_constant<int, 0>{});
     if (i0 < T - 1) step(i0++, std::integral_constant<int, 1>{});
     const int i = T - 1;
-    vector_phase<kD, true>(s, qs, ksc, c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
+    vector_phase<kD, true, kDump>(s, qs, ksc, c, log2_448, Skv - i * kKeyTile, g, st, o, pop, prow_at(i));
     pv_tile<kD>(lds_v[i % 3], pop, li, g, o);
   } else {
     // (slot-instantiated body as above; the scales of tile i load at the
@@ -492,7 +499,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
       qk_tile<kD>(lds_k[sl], qf, li, g, bias, s);
       if (i > 0) pv_tile<kD>(lds_v[(sl + 2) % 3], pop, li, g, o);
       __builtin_amdgcn_s_setprio(0);
-      vector_phase<kD, false>(s, qs, ksc, c, log2_448, kKeyTile, g, st, o, pop);
+      vector_phase<kD, false, kDump>(s, qs, ksc, c, log2_448, kKeyTile, g, st, o, pop, prow_at(i));
       wait_tiles();
       __syncthreads();
     };
@@ -509,7 +516,7 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
     if (i > 0) pv_tile<kD>(lds_v[(sl + 2) % 3], pop, li, g, o);
     qk_tile<kD>(lds_k[sl], qf, li, g, bias, s);
     const float4 ksc = *(const float4*)(ksb + i * (kKeyTile / kQBlock));
-    vector_phase<kD, true>(s, qs, ksc, c, log2_448, Skv - i * kKeyTile, g, st, o, pop);
+    vector_phase<kD, true, kDump>(s, qs, ksc, c, log2_448, Skv - i * kKeyTile, g, st, o, pop, prow_at(i));
     pv_tile<kD>(lds_v[sl], pop, li, g, o);
   }
 

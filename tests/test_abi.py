@@ -118,6 +118,13 @@ def test_validation_codes():
     assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 128, 0, 0, 0, 256, 0, 257, f, z) == ERR_RANGE
     assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 128, 0, 2, 0, 1, 0, 1, f, z) == ERR_RANGE
     assert _call("sage_debug_qk_scores", f, f, 1, 256, 2, 128, 0, 0, 0, 0, 0, 1, f, z) == ERR_RANGE
+    # P-code dump: same checks as sage_attn_fwd, plus the codes buffer and the sequence limit
+    c01 = ctypes.c_float(0.1)
+    assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 256, 2, 128, c01, z, f, z) == ERR_NULL
+    assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 256, 2, 96, c01, f, f, z) == ERR_UNSUP
+    assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 16385, 2, 128, c01, f, f, z) == ERR_RANGE
+    assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 256, 2, 128, ctypes.c_float(-1.0), f, f, z) == ERR_SHAPE
+    assert _call("sage_debug_p_codes", m, f, f, f, f, f, 1, 256, 2, 128, c01, f, f, z) == ERR_ALIGN
 
 
 def test_extended_entry_points_validation():

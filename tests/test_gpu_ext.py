@@ -128,30 +128,6 @@ def test_attention_ex_one_shot(idx, Sq, Skv, H, flags):
     lse_gate(lse.cpu().numpy(), rlse, f"flags={flags}")
 
 
-def test_attention_ex_lse_full_size_sampled():
-    """Image-DiT 2048^2 (B=1, S=16384, H=24) through sage_attention_ex with the
-    LSE, in the launch configuration the benchmark times; sampled rows of
-    three heads against the oracle row by row."""
-    cfg = workloads.config(3)
-    _say("attention_ex with LSE at B=1 S=16384 H=24; generating inputs")
-    q, k, v = workloads.generate(3, chunk_elems=1 << 26)
-    out, lse = sage.sage_attention_ex(to_dev(q), to_dev(k), to_dev(v), cfg.softmax_scale, return_lse=True)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(33)
-    bn = sage.sage_kv_tile()
-    for b, h in [(0, 0), (0, 23), (0, int(rng.integers(24)))]:
-        rows = np.unique(np.concatenate([np.arange(32), np.arange(cfg.S - 32, cfg.S), rng.choice(cfg.S, 256, replace=False)]))
-        sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1, :])  # noqa: E731
-        q8, qs = oracle.quant_qk(sl(q))
-        k8, ks = oracle.quant_qk(sl(k))
-        v8, vs = oracle.quant_v(sl(v))
-        ro, rl = oracle.attention_head(q8[0, 0], qs[0, 0], k8[0, 0], ks[0, 0], v8[0, 0], vs[0, 0],
-                                       cfg.softmax_scale, bn, rows=rows, return_lse=True)
-        g = out[b, torch.as_tensor(rows, device=DEV), h, :].float().cpu().numpy()
-        gate(g, ro, None, f"(b,h)=({b},{h}) rows={len(rows)}")
-        lse_gate(lse[b, h, torch.as_tensor(rows, device=DEV)].cpu().numpy(), rl, f"(b,h)=({b},{h})")
-
-
 # --------------------------------------------------------------------------
 # Q quantized inside the attention kernel
 

@@ -191,6 +191,45 @@ def test_debug_scores_extreme_codes():
     assert np.array_equal(got.cpu().numpy(), ref)
 
 
+def test_p_codes_flip_count_config1():
+    """The FP8 codes of P the kernel forms, per key tile against the running
+    maximum, against the oracle's (its tile loop with a trace): a diagnostic
+    of how often fp32 rounding differences (the hardware exp2, summation
+    order) move a code to its neighbour. The dump run's output equals
+    sage_attn_fwd's bit for bit."""
+    _say("P codes, config 1")
+    cfg = workloads.config(1)
+    q, k, v = workloads.generate(1)
+    B, S, H, D = q.shape
+    r = run_split(q, k, v, cfg.softmax_scale)
+    out, codes = sage.sage_debug_p_codes(r["q8"], r["qs"], r["k8"], r["ks"], r["v8"], r["vs"], B, S, H, D,
+                                         cfg.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), r["out"].view(torch.int16))
+    got = codes.cpu().numpy()
+    assert np.all(got[..., S:] == 0)
+    oq, oqs = oracle.quant_qk(q)
+    ok, oks = oracle.quant_qk(k)
+    ov, ovs = oracle.quant_v(v)
+    bn = sage.sage_kv_tile()
+    total = flips = 0
+    for h in range(H):
+        A = oracle.qk_scores(oq[0, h], ok[0, h])
+        c = oracle.exp2_scale(cfg.softmax_scale)
+        fb = (oqs[0, h][:, None].astype(np.float32) * oks[0, h][None, :].astype(np.float32)).astype(np.float32)
+        f = (fb * c).astype(np.float32)[np.arange(S)[:, None] // 32, np.arange(S)[None, :] // 32]
+        trace = []
+        oracle.online_softmax_pv(A, f, oracle.fp8_e4m3fn_decode(ov[0, h]), bn, trace=trace)
+        ref = np.concatenate([t["p8"] for t in trace], axis=1)
+        g = got[0, h, :, :S]
+        d = g.astype(np.int64) - ref.astype(np.int64)
+        total += d.size
+        flips += int(np.count_nonzero(d))
+        assert np.abs(d).max() <= 1, h          # a flip moves a code to its neighbour
+    _say(f"  P codes: {flips} of {total} differ from the oracle's ({flips / total:.2e})")
+    assert flips <= 1e-4 * total
+
+
 # --------------------------------------------------------------------------
 # attention output
 
@@ -242,29 +281,6 @@ def _sample_rows(S, rng, nrand=2, nrows=1024):
     rows = np.concatenate([np.arange(32 * t, min(S, 32 * t + 32)) for t in blocks]
                           + [rng.choice(S, nrows, replace=False)])
     return np.unique(rows)
-
-
-@pytest.mark.parametrize("idx", [3, 4, 5])
-def test_attention_full_size_sampled(idx):
-    cfg = workloads.config(idx)
-    _say(f"attention config {idx} ({cfg.name}), sampled compare; generating inputs")
-    q, k, v = workloads.generate(idx, chunk_elems=1 << 26)
-    rng = np.random.default_rng(idx)
-    _say("  running the GPU path (one-shot sage_attention)")
-    out = sage.sage_attention(to_dev(q), to_dev(k), to_dev(v), cfg.softmax_scale)
-    torch.cuda.synchronize()
-    got = out.float().cpu().numpy() if idx != 5 else None
-    pairs = [(0, 0), (cfg.B - 1, cfg.H - 1), (int(rng.integers(cfg.B)), int(rng.integers(cfg.H)))]
-    for b, h in pairs:
-        rows = _sample_rows(cfg.S, rng)
-        g = got[b, rows, h, :] if got is not None else out[b, torch.as_tensor(rows, device=DEV), h, :].float().cpu().numpy()
-        ref = oracle_rows(q, k, v, b, h, rows, cfg.softmax_scale, sage.sage_kv_tile())
-        ex = exact_rows(q, k, v, b, h, rows, cfg.softmax_scale)
-        gate(g, ref, ex, f"config {idx} (b,h)=({b},{h}) rows={len(rows)}")
-    if got is not None:
-        assert np.all(np.isfinite(got))
-    else:
-        assert bool(torch.isfinite(out).all())
 
 
 def test_one_shot_equals_split_and_is_deterministic():
