@@ -26,7 +26,11 @@ Readings taken where the pages are silent, in step order:
    the fewest roundings; the two-step fl32(t_j - m2_tau) differs from it by
    at most half an ulp of t_j); P'_j = fl32(2^arg_j), so P'_j = 448 *
    2^(t_j - m_tau) up to rounding. p8_j = E4M3FN(P'_j) (saturating at 448).
-   The row sum l accumulates the fp32 P'_j.
+   The row sum l accumulates the decoded codes dec(p8_j): the normalizer is
+   the sum of the very weights that multiply V, so the quantized weights of a
+   row sum to one (the fp32 P'_j would leave them off by the FP8 rounding
+   noise). Diffusers issue #15014 (problem statement) fixes only that the
+   softmax runs in fp32, not which of the two sums normalizes.
 5. Across tiles, partial sums are combined with the factors 2^(m2_tau -
    m2_T) of the final tile T (here in float64; a kernel rescales its fp32
    accumulators as it goes, which agrees to fp32 rounding).
@@ -102,8 +106,9 @@ def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None, with_shif
     vals: float64 [S, D] decoded FP8 V values (natural key order).
     bn:   key tile width; keys at index >= n_valid are masked.
     Returns (acc float64 [R, D], l float64 [R]); the output is
-    acc * v_scale / l. With ``with_shift`` also m2 of the last tile (float64
-    holding fp32 values): l = sum_j 2^(t_j - m2_T) up to rounding. With a
+    acc * v_scale / l, with l = sum_j dec(p8_j) 2^(m2_tau(j) - m2_T). With
+    ``with_shift`` also m2 of the last tile (float64 holding fp32 values):
+    l = sum_j 2^(t_j - m2_T) up to the FP8 rounding of each term. With a
     ``trace`` list, one dict per tile (j0, j1, m2, arg, p, p8) is appended
     to it (used by the tests that pin the exponent step).
     """
@@ -127,7 +132,7 @@ def online_softmax_pv(A, f, vals, bn: int, n_valid: int | None = None, with_shif
         if trace is not None:
             trace.append(dict(j0=j0, j1=j1, m2=m2, arg=arg, p=p, p8=p8))
         shifts.append(m2.astype(np.float64))
-        l_parts.append(p.astype(np.float64).sum(axis=1))
+        l_parts.append(p_used.sum(axis=1))
         acc_parts.append(p_used @ np.asarray(vals[j0:j1], dtype=np.float64))
         m_prev = m
     return _combine(shifts, l_parts, acc_parts, vals.shape[1], with_shift)
@@ -159,7 +164,8 @@ def online_softmax_exact(x, vals, bn: int, n_valid: int | None = None):
 def lse_from_state(m2_final, l):
     """Log-sum-exp of a row's scaled scores from the online-softmax state.
 
-    l = sum_j 2^(t_j - m2_T) with t_j = softmax_scale * log2(e) * score_j, so
+    l = sum_j 2^(t_j - m2_T) up to the FP8 rounding of each term (l sums the
+    decoded codes), with t_j = softmax_scale * log2(e) * score_j, so
     ln sum_j exp(softmax_scale * score_j) = ln 2 * (m2_T + log2 l). Formed in
     float64 and rounded once to fp32 (the output type). Reading: the pages
     only say that ring attention needs the LSE (diffusers PR #15060, "What

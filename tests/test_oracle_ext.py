@@ -174,6 +174,7 @@ def test_oracle_lse_matches_dequantized_logsumexp(idx, Sq, Skv):
     q8, qs = quant_qk(q)
     k8, ks = quant_qk(k)
     v8, vs = quant_v(v)
+    errs = []
     for h in range(q.shape[2]):
         _, lse = attention_head(q8[0, h], qs[0, h], k8[0, h], ks[0, h], v8[0, h], vs[0, h],
                                 cfg.softmax_scale, 128, return_lse=True)
@@ -181,15 +182,25 @@ def test_oracle_lse_matches_dequantized_logsumexp(idx, Sq, Skv):
         deq = (A * qs[0, h][np.arange(Sq) // 32][:, None].astype(np.float64)
                * ks[0, h][np.arange(Skv) // 32][None, :].astype(np.float64))
         ref = logsumexp(deq * cfg.softmax_scale, axis=1)
-        # each exponent carries fp32 roundings of about one unit of f (the
-        # per-block factor in the log2 domain), plus fp32 rounding of c, f
-        # and the result
+        # l sums the decoded FP8 codes of P' = 2^(t - m2): each is P' (1 +
+        # eta) with |eta| <= 2^-4 in the normal range, or P' + zeta with
+        # |zeta| <= 2^-10 below it, and l >= ~448 (the row's largest term),
+        # so ln l is within ln(1 + 2^-4 + Skv 2^-10 / 448) of the exact sum's
+        # logarithm; each exponent also carries fp32 roundings of about one
+        # unit of f (the per-block factor in the log2 domain)
         f = (qs[0, h][np.arange(Sq) // 32][:, None].astype(np.float64)
              * ks[0, h][None, :].astype(np.float64) * cfg.softmax_scale * math.log2(math.e))
         fmax = f.max(axis=1)
         tmax = np.abs(deq).max(axis=1) * cfg.softmax_scale * math.log2(math.e)
-        bound = math.log(2.0) * (2.5 * fmax + 8 * U32 * (tmax + 30)) + 4 * U32 * np.abs(ref)
-        assert np.all(np.abs(lse.astype(np.float64) - ref) <= bound), h
+        bound = (math.log1p(2.0 ** -4 + Skv * 2.0 ** -10 / 448)
+                 + math.log(2.0) * (2.5 * fmax + 8 * U32 * (tmax + 30)) + 4 * U32 * np.abs(ref))
+        err = lse.astype(np.float64) - ref
+        assert np.all(np.abs(err) <= bound), h
+        errs.append(err)
+    # the FP8 roundings go either way: their mean effect over the rows is far
+    # smaller than their per-row bound (measured 1e-4 to 7e-4 on these
+    # inputs), which pins a systematic offset of the LSE
+    assert abs(np.mean(np.concatenate(errs))) <= 2e-3
 
 
 def test_planted_lse_mistakes_fail_the_pin(monkeypatch):
