@@ -171,9 +171,14 @@ sage_status sage_quant_v_noalloc(const void* v, int64_t B, int64_t S, int64_t H,
  *   m2 = fl32(m - fl32(log2 448)); P' = 2^fl32(A*f - m2), the exponent
  *   being the exact real value A*f - m2 rounded once (a fused multiply-add;
  *   hardware exp2), so P' = 448 * 2^(t - m) up to rounding;
- *   l = sum of fp32 P' (rescaled by 2^(m2_old - m2) when the max moves);
- *   p8 = E4M3FN(min(P', 448)); acc[c] = sum p8 * v8[c] (FP8 MFMA, fp32
- *   accumulation, same rescaling); out = bf16_rne(acc * v_scale[c] / l).
+ *   p8 = E4M3FN(min(P', 448)); acc[c] = sum p8 * v8[c] and l = sum p8
+ *   (FP8 MFMAs, fp32 accumulation, rescaled by 2^(m2_old - m2) when the max
+ *   moves): the normalizer sums the same FP8 weights that multiply V;
+ *   out = bf16_rne(acc * v_scale[c] / l).
+ * The FP8 MFMA adds its exact products after cutting each to a grid set by
+ * the largest exponents in its group of 8 (sage_debug_fp8_dot), so l can be
+ * below the exact sum of the codes by less than 7 * 2^-13 of it, and each
+ * element of acc off by less than 7 * 2^-13 * max|v8[c]| * (l + S / 512).
  */
 sage_status sage_attn_fwd(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                           const float* k_scale, const uint8_t* v_fp8_t, const float* v_scale,
@@ -197,8 +202,7 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
  * of one (b, h), rows [r0, r0+nr) x keys [c0, c0+nc), computed through the
  * attention kernel's own path: K tiles staged into LDS by the same
  * buffer-to-LDS copies into the same swizzled layout, the same Q fragments,
- * the same INT8 MFMA sequence with the accumulators starting from the bias
- * 0x4B400000, which is subtracted when a score is stored.
+ * the same INT8 MFMA sequence with the accumulators starting from zero.
  *   scores  int32 [nr, nc] out, row-major.
  * Windows must satisfy 0 <= r0, 0 < nr, r0+nr <= S_pad (same for keys).
  * D is 128 or 64.
@@ -225,6 +229,25 @@ sage_status sage_debug_p_codes(const int8_t* q_i8, const float* q_scale, const i
                                const float* k_scale, const uint8_t* v_fp8_t, const float* v_scale,
                                int64_t B, int64_t S, int64_t H, int64_t D, float softmax_scale,
                                uint8_t* codes, void* out, void* stream);
+
+/*
+ * sage_debug_fp8_dot - debug run of the FP8 MFMA of the PV step (FP8 PV with
+ * fp32 accumulation, diffusers issue #15014 problem statement) on n given
+ * pairs of E4M3FN vectors of 64 codes: out[c] = init[c] + a[c] . b[c], where
+ * a takes the place of a V^T row and b that of a column of P.
+ *   a, b  uint8 [n, 64] in, 16-byte aligned, device; consumed in groups of 8
+ *         consecutive codes.
+ *   init  fp32 [n] in, device: the accumulator before the MFMA.
+ *   out   fp32 [n] out, device.
+ * The products are exact but their sum is not: in each group of 8 the MFMA
+ * cuts every product toward zero to a multiple of 2^(E-13), where E is the
+ * largest e_a + e_b over the group's non-zero products and e is the exponent
+ * of an operand's encoding (-6 for subnormals), then adds the group sums and
+ * init in fp32.
+ * 1 <= n <= 2^24 (SAGE_ERR_RANGE otherwise). Test and diagnostic use only.
+ */
+sage_status sage_debug_fp8_dot(const uint8_t* a, const uint8_t* b, int64_t n, const float* init, float* out,
+                               void* stream);
 
 /* ---------------------------------------------------------------------------
  * Extensions beyond the gfx1201 operation: log-sum-exp output, query and
@@ -275,7 +298,10 @@ sage_status sage_quant_k_smooth(const void* k, int64_t B, int64_t S, int64_t H, 
  *   lse  fp32 [B, H, Sq] or NULL (4-byte aligned): per query row,
  *        ln(sum_j exp(softmax_scale * q.k_j)) of the dequantized scores,
  *        formed from the kernel's state as ln2 * (m2 + log2 l) (m2 and l as
- *        in sage_attn_fwd after the last key tile).
+ *        in sage_attn_fwd after the last key tile; l sums the FP8 codes of
+ *        P, so this is the exact value up to their rounding, at most
+ *        ln(1 + 2^-4) per row and unbiased on average, and up to the FP8
+ *        MFMA's cuts, which lower it by less than 8.6e-4).
  * sage_attn_fwd(..., S, ...) equals sage_attn_fwd_ex(..., S, S, ..., NULL).
  */
 sage_status sage_attn_fwd_ex(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8, const float* k_scale,

@@ -21,7 +21,7 @@ __all__ = [
     "sage_attn_fwd", "sage_attention", "sage_debug_qk_scores", "v_key_order",
     "SAGE_SMOOTH_K", "sage_k_smooth_scratch_bytes", "sage_quant_k_smooth", "sage_attn_fwd_ex",
     "sage_workspace_bytes_ex", "sage_attention_ex", "sage_attn_fwd_qbf16", "sage_quant_v_noalloc",
-    "sage_quant_kv", "sage_debug_p_codes",
+    "sage_quant_kv", "sage_debug_p_codes", "sage_debug_fp8_dot",
 ]
 
 SAGE_SMOOTH_K = 1
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         "sage_debug_qk_scores": (ctypes.c_int, [p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                                 i64, p, p]),
         "sage_debug_p_codes": (ctypes.c_int, [p, p, p, p, p, p, i64, i64, i64, i64, f32, p, p, p]),
+        "sage_debug_fp8_dot": (ctypes.c_int, [p, p, i64, p, p, p]),
         "sage_k_smooth_scratch_bytes": (sz, [i64, i64, i64, i64]),
         "sage_quant_k_smooth": (ctypes.c_int, [p, i64, i64, i64, i64, p, p, p, p, sz, p]),
         "sage_attn_fwd_ex": (ctypes.c_int, [p, p, p, p, p, p, i64, i64, i64, i64, i64, f32, p, p, p]),
@@ -319,6 +320,27 @@ def sage_debug_p_codes(q_i8, q_scale, k_i8, k_scale, v_fp8_t, v_scale, B, S, H, 
                                     _ptr(v_scale), B, S, H, D, float(softmax_scale), _ptr(codes), _ptr(out),
                                     _stream_ptr(stream)))
     return out, codes
+
+
+def sage_debug_fp8_dot(a, b, init=None, out=None, stream=None):
+    """init + a[c] . b[c] for each row pair of a and b (uint8 E4M3FN codes,
+    [n, 64]) through the PV step's FP8 MFMA. Returns fp32 [n]."""
+    torch = _torch()
+    _require(a, torch.uint8, "a")
+    _require(b, torch.uint8, "b")
+    if a.dim() != 2 or a.shape[1] != 64 or b.shape != a.shape:
+        raise ValueError("a and b must both be [n, 64]")
+    n = a.shape[0]
+    if init is None:
+        init = torch.zeros(n, dtype=torch.float32, device=a.device)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=a.device)
+    _require(init, torch.float32, "init")
+    _require(out, torch.float32, "out")
+    if init.numel() < n or out.numel() < n:
+        raise ValueError("init or out too small")
+    _check(lib().sage_debug_fp8_dot(_ptr(a), _ptr(b), n, _ptr(init), _ptr(out), _stream_ptr(stream)))
+    return out
 
 
 def sage_k_smooth_scratch_bytes(B, S, H, D=128) -> int:

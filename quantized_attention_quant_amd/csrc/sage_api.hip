@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kAbiVersion = 1;
 constexpr int64_t kDebugPMaxSeq = 16384;  // sage_debug_p_codes: S x S_pad bytes per head
+constexpr int64_t kDebugDotMax = int64_t(1) << 24;  // sage_debug_fp8_dot pairs
 thread_local char g_last_error[512] = "";
 
 sage_status fail(sage_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -507,6 +508,20 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
                        st, q_i8, k_i8, (int)Sp, b * H + h, (int)rA, (int)r0, (int)nr, (int)cA, (int)c0, (int)nc,
                        scores);
   return launched("sage_debug_qk_scores");
+}
+
+sage_status sage_debug_fp8_dot(const uint8_t* a, const uint8_t* b, int64_t n, const float* init, float* out,
+                               void* stream) {
+  SAGE_TRY(check_ptr(a, "a"));
+  SAGE_TRY(check_ptr(b, "b"));
+  if (!init) return fail(SAGE_ERR_NULL, "init is NULL");
+  if (!out) return fail(SAGE_ERR_NULL, "out is NULL");
+  if ((((uintptr_t)init) | ((uintptr_t)out)) & 3) return fail(SAGE_ERR_ALIGN, "init or out is not 4-byte aligned");
+  if (n < 1 || n > kDebugDotMax) return fail(SAGE_ERR_RANGE, "n must be in [1, %lld]", (long long)kDebugDotMax);
+  if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
+  hipLaunchKernelGGL(sage::debug_fp8_dot_kernel, dim3((unsigned)((n + 31) / 32)), dim3(64), 0, (hipStream_t)stream,
+                     a, b, n, init, out);
+  return launched("sage_debug_fp8_dot");
 }
 
 size_t sage_k_smooth_scratch_bytes(int64_t B, int64_t S, int64_t H, int64_t D) {

@@ -7,11 +7,17 @@ than the oracle minus 1e-4 (inputs whose quantization loses the scores, such
 as a +600 Q/K channel). Every call prints its maxima, so that a log shows how
 far each case is from its bound.
 
-The LSE gate: |lse_gpu - lse_oracle| <= 4e-5 + 1e-6 |lse_oracle|. The two
-sides differ by the fp32 summation order of l (at most a few hundred
-roundings along a row's chain, each 2^-24 relative: <= 2e-5 in ln l), the
-hardware log2 (about 1 ulp) and the final fp32 roundings of m2 + log2 l and
-of the product with ln 2.
+The LSE gate: -(ln(1 / (1 - 7 * 2^-13)) + r) <= lse_gpu - lse_oracle <= r,
+with r = 4e-5 + 1e-6 |lse_oracle|. The oracle sums the decoded FP8 codes of P
+exactly; the kernel sums them with an FP8 MFMA and an all-ones operand, which
+within each group of 8 codes cuts every code toward zero to a multiple of
+2^(E-13), E the exponent of the group's largest code (the rule is pinned in
+test_gpu_fp8_mfma.py). Each group keeps more than 1 - 7 * 2^-13 of its sum, so
+the kernel's l is low by at most that fraction and its LSE by at most
+8.55e-4. The symmetric part r
+covers the fp32 additions and rescalings along a row's chain (each 2^-24
+relative: <= 2e-5 in ln l), the hardware log2 (about 1 ulp) and the final
+fp32 roundings of m2 + log2 l and of the product with ln 2.
 """
 import sys
 
@@ -59,14 +65,19 @@ def gate(got, ref, exact=None, label=""):
             assert c_gpu >= c_ora - 1e-4, label
 
 
+LSE_CUT = -np.log1p(-7 * 2.0 ** -13)     # the row-sum MFMA's largest loss, in ln l
+
+
 def lse_gate(got, ref, label=""):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert np.all(np.isfinite(got)), label
-    err = np.abs(got - ref)
-    bound = 4e-5 + 1e-6 * np.abs(ref)
-    say(f"  {label}: lse max|err| {err.max():.3g} (bound at that row {bound.ravel()[err.argmax()]:.3g})")
-    assert np.all(err <= bound), label
+    d = got - ref
+    r = 4e-5 + 1e-6 * np.abs(ref)
+    say(f"  {label}: lse - oracle in [{d.min():.3g}, {d.max():.3g}] "
+        f"(bounds [-{LSE_CUT:.3g} - r, r], r <= {r.max():.3g}), mean {d.mean():.3g}")
+    assert np.all(d <= r), label
+    assert np.all(d >= -(LSE_CUT + r)), label
 
 
 def kappa(p):

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     for n in ("sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_attention", "sage_debug_qk_scores",
               "sage_workspace_bytes", "sage_kv_tile", "sage_seq_pad", "sage_quant_k_smooth",
               "sage_k_smooth_scratch_bytes", "sage_attn_fwd_ex", "sage_workspace_bytes_ex",
-              "sage_attention_ex"):
+              "sage_attention_ex", "sage_debug_p_codes", "sage_debug_fp8_dot"):
         assert n in names
 
 
@@ -125,7 +125,16 @@ def test_validation_codes():
     assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 16385, 2, 128, c01, f, f, z) == ERR_RANGE
     assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 256, 2, 128, ctypes.c_float(-1.0), f, f, z) == ERR_SHAPE
     assert _call("sage_debug_p_codes", m, f, f, f, f, f, 1, 256, 2, 128, c01, f, f, z) == ERR_ALIGN
-
+    # FP8 MFMA probe: pointers, alignment, pair count
+    assert _call("sage_debug_fp8_dot", z, f, 1, f, f, z) == ERR_NULL
+    assert _call("sage_debug_fp8_dot", f, z, 1, f, f, z) == ERR_NULL
+    assert _call("sage_debug_fp8_dot", f, f, 1, z, f, z) == ERR_NULL
+    assert _call("sage_debug_fp8_dot", f, f, 1, f, z, z) == ERR_NULL
+    assert _call("sage_debug_fp8_dot", m, f, 1, f, f, z) == ERR_ALIGN
+    assert _call("sage_debug_fp8_dot", f, m, 1, f, f, z) == ERR_ALIGN
+    assert _call("sage_debug_fp8_dot", f, f, 1, f, p(FAKE + 2), z) == ERR_ALIGN
+    assert _call("sage_debug_fp8_dot", f, f, 0, f, f, z) == ERR_RANGE
+    assert _call("sage_debug_fp8_dot", f, f, (1 << 24) + 1, f, f, z) == ERR_RANGE
 
 def test_extended_entry_points_validation():
     p = ctypes.c_void_p

@@ -1,0 +1,200 @@
+"""How the PV step's FP8 MFMA adds its products, pinned on given codes.
+
+PV multiplies FP8 codes of V^T and P on the FP8 MFMA with fp32 accumulation,
+and the row sum l adds the FP8 codes of P on the same instruction with an
+all-ones operand. Each product of two FP8 values is exact, but the MFMA does
+not add the 64 products of a call exactly:
+
+* it works on groups of 8 consecutive codes;
+* E is the largest exponent sum e_a + e_b over the group's non-zero
+  products, where e is the exponent of an operand's encoding (-6 for
+  subnormals), not the exponent of the product's value;
+* every product of the group is cut toward zero to a multiple of 2^(E-13);
+* the group sums and the accumulator are added in fp32.
+
+These tests pin that model through sage_debug_fp8_dot, which runs the same
+instruction on n pairs of vectors:
+
+* hand-made pairs that show each part of it;
+* random signed codes, and the V^T and P codes of a real attention run,
+  against the model within fp32 rounding;
+* the bound for sums of non-negative codes with an all-ones operand (the
+  row sum l): the MFMA's sum lies in [(1 - 7 * 2^-13) * exact, exact], up
+  to fp32 rounding.
+
+For PV the cut lowers each output element by less than 7 * 2^-13 of the
+channel's max|V| (and less than that again for the subnormal codes), about
+8.5e-4: a twelfth of the output tolerance.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+sage = pytest.importorskip("quantized_attention_quant_amd")
+from gpu_common import DEV, say, to_dev, unpermute_vt  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+GROUP = 8
+GRID_BITS = 13
+LOSS = 7 * 2.0 ** -GRID_BITS          # largest fraction of a group's magnitude the cuts remove
+F32_ADDS = 9 * 2.0 ** -24             # the group sums and init added in fp32
+FINITE = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)   # E4M3FN codes except NaN
+
+
+def _code(x):
+    return int(oracle.fp8_e4m3fn_encode(np.array([x]))[0])
+
+
+def _dec(codes):
+    return oracle.fp8_e4m3fn_decode(codes).astype(np.float64)
+
+
+def _exp_field(codes):
+    """Exponent of an E4M3FN encoding: field - 7, and -6 for subnormals."""
+    return np.maximum(((codes.astype(np.int64) >> 3) & 15) - 7, -6)
+
+
+def model_dot(a, b, init, toward_zero=True, grid_from="encodings"):
+    """init + the group-cut sum of a[c] * b[c] (uint8 [n, 64] each), fp64,
+    and the sum of the magnitudes of the terms (for the rounding bound).
+
+    The model pinned here is the default. The other choices exist to report
+    how far the hardware is from them: cutting toward -inf instead of toward
+    zero, or taking E from the exponent of the largest product's value."""
+    n = a.shape[0]
+    prod = (_dec(a) * _dec(b)).reshape(n, -1, GROUP)
+    mag = np.abs(prod)
+    if grid_from == "encodings":
+        esum = (_exp_field(a) + _exp_field(b)).reshape(prod.shape)
+        e = np.where(prod != 0, esum, -99).max(axis=2, keepdims=True)
+    else:
+        big = mag.max(axis=2, keepdims=True)
+        e = np.floor(np.log2(np.where(big > 0, big, 1.0)))
+    grid = np.exp2(e - GRID_BITS)
+    if toward_zero:
+        cut = np.sign(prod) * np.floor(mag / grid) * grid
+    else:
+        cut = np.floor(prod / grid) * grid
+    return init.astype(np.float64) + cut.sum(axis=(1, 2)), np.abs(init) + np.abs(cut.sum(axis=2)).sum(axis=1)
+
+
+def _run(a, b, init):
+    got = sage.sage_debug_fp8_dot(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV),
+                                  torch.from_numpy(init).to(DEV))
+    torch.cuda.synchronize()
+    return got.cpu().numpy().astype(np.float64)
+
+
+def test_fp8_mfma_hand_cases():
+    say("FP8 MFMA: hand-made pairs")
+    cases = []   # (description, {index: (a, b)}, init, expected)
+
+    def case(desc, terms, init, want):
+        cases.append((desc, {i: (t if isinstance(t, tuple) else (1.0, t)) for i, t in terms.items()}, init, want))
+
+    case("448 + 2^-6 in one group: below the 2^-5 grid of 448", {0: 448.0, 1: 2.0 ** -6}, 0.0, 448.0)
+    case("448 + 2^-6 in the next group: kept", {0: 448.0, 8: 2.0 ** -6}, 0.0, 448.0 + 2.0 ** -6)
+    case("448 + 2^-5: on the grid", {0: 448.0, 7: 2.0 ** -5}, 0.0, 448.0 + 2.0 ** -5)
+    case("448 + 1.75 x 2^-5: cut toward zero", {0: 448.0, 1: 1.75 * 2.0 ** -5}, 0.0, 448.0 + 2.0 ** -5)
+    case("448 - 1.75 x 2^-5: cut toward zero", {0: 448.0, 1: -1.75 * 2.0 ** -5}, 0.0, 448.0 - 2.0 ** -5)
+    case("-448 - 2^-6: cut toward zero", {0: -448.0, 1: -(2.0 ** -6)}, 0.0, -448.0)
+    case("16 + 2^-9 (grid 2^-9)", {0: 16.0, 1: 2.0 ** -9}, 0.0, 16.0 + 2.0 ** -9)
+    case("64 + 2^-8 (grid 2^-7)", {0: 64.0, 1: 2.0 ** -8}, 0.0, 64.0)
+    case("1.75 x 1.75 = 3.0625 + 2^-13: E = 0 + 0 from the encodings, not 1 from the value",
+         {0: (1.75, 1.75), 1: (2.0 ** -4, 2.0 ** -9)}, 0.0, 3.0625 + 2.0 ** -13)
+    case("1.75 x 1.75 + 2^-14: below that grid", {0: (1.75, 1.75), 1: (2.0 ** -5, 2.0 ** -9)}, 0.0, 3.0625)
+    case("2^-9 x 448 + 2^-12: a subnormal counts at exponent -6 (E = 2)",
+         {0: (2.0 ** -9, 448.0), 1: (2.0 ** -6, 2.0 ** -6)}, 0.0, 0.875)
+    case("0 x 448 + 2^-18: a zero product does not set E", {0: (0.0, 448.0), 1: (2.0 ** -9, 2.0 ** -9)}, 0.0,
+         2.0 ** -18)
+    case("448 + 63 x 2^-9: the 7 in 448's group are lost",
+         {0: 448.0, **{i: 2.0 ** -9 for i in range(1, 64)}}, 0.0, 448.0 + 56 * 2.0 ** -9)
+    case("init 2^20 + 1.0: init kept at fp32 precision", {0: 1.0}, 2.0 ** 20, 2.0 ** 20 + 1.0)
+    case("init 2^-9 + 448: init is not on the group grid", {0: 448.0}, 2.0 ** -9, 448.0 + 2.0 ** -9)
+    case("64 x 448 x 448", {i: (448.0, 448.0) for i in range(64)}, 0.0, 64 * 448.0 * 448.0)
+    case("64 x 2^-9 x 2^-9", {i: (2.0 ** -9, 2.0 ** -9) for i in range(64)}, 0.0, 64 * 2.0 ** -18)
+    n = len(cases)
+    a = np.zeros((n, 64), np.uint8)
+    b = np.zeros((n, 64), np.uint8)
+    init = np.zeros(n, np.float32)
+    for c, (_, terms, ini, _) in enumerate(cases):
+        for i, (x, y) in terms.items():
+            a[c, i], b[c, i] = _code(x), _code(y)
+            assert _dec(np.array([a[c, i]]))[0] == x and _dec(np.array([b[c, i]]))[0] == y
+        init[c] = ini
+    got = _run(a, b, init)
+    want, _ = model_dot(a, b, init)
+    for c, (desc, _, _, expected) in enumerate(cases):
+        say(f"  {desc}: got {float(got[c])!r}, expected {float(expected)!r}")
+        assert want[c] == expected, desc          # the model states each case
+        assert got[c] == expected, desc
+
+
+def _check_against_model(a, b, init, label):
+    got = _run(a, b, init)
+    want, scale = model_dot(a, b, init)
+    err = np.abs(got - want)
+    others = {"cut toward -inf": model_dot(a, b, init, toward_zero=False)[0],
+              "E from the largest product's value": model_dot(a, b, init, grid_from="value")[0],
+              "exact sum": init.astype(np.float64) + (_dec(a) * _dec(b)).sum(axis=1)}
+    far = {k: int(np.count_nonzero(np.abs(got - v) > F32_ADDS * scale)) for k, v in others.items()}
+    say(f"  {label}: n={len(got)}, max |got - model| / scale {np.max(err / np.maximum(scale, 1e-30)):.3g}; "
+        f"pairs off the other models by more than fp32 rounding: {far}")
+    assert np.all(err <= F32_ADDS * scale), label
+    return got
+
+
+def test_fp8_mfma_random_signed_codes_follow_the_model():
+    say("FP8 MFMA: random signed codes")
+    rng = np.random.default_rng(7)
+    n = 1 << 14
+    a = rng.choice(FINITE, size=(n, 64))
+    b = rng.choice(FINITE, size=(n, 64))
+    init = np.where(rng.random(n) < 0.5, 0.0, rng.normal(0.0, 1000.0, n)).astype(np.float32)
+    _check_against_model(a, b, init, "uniform finite codes")
+
+
+def test_fp8_mfma_nonnegative_sums_lose_at_most_seven_grid_steps():
+    say("FP8 MFMA: sums of non-negative codes (all-ones a)")
+    rng = np.random.default_rng(8)
+    n = 1 << 14
+    b = rng.integers(0, 0x7F, size=(n, 64), dtype=np.uint8)
+    half = n // 2
+    b[half:] = oracle.fp8_e4m3fn_encode(448.0 * np.exp2(-rng.exponential(4.0, size=(half, 64)))).astype(np.uint8)
+    a = np.full((n, 64), _code(1.0), np.uint8)
+    init = np.zeros(n, np.float32)
+    got = _check_against_model(a, b, init, "one large weight and many small ones")
+    exact = _dec(b).sum(axis=1)
+    lost = (exact - got) / np.maximum(exact, 1e-30)
+    say(f"  lost fraction of the exact sum: max {lost.max():.3g} (bound {LOSS:.3g}), min {lost.min():.3g}")
+    assert np.all(lost <= LOSS + F32_ADDS)
+    assert np.all(lost >= -F32_ADDS)
+
+
+def test_fp8_mfma_on_attention_codes():
+    say("FP8 MFMA: V^T and P codes of an attention run (outlier recipe, S=600)")
+    S, H, D = 600, 2, 128
+    q, k, v = workloads.generate(3, S=S, H=H, B=1, seed=11)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    q8, qs = sage.sage_quant_qk(qd)
+    k8, ks = sage.sage_quant_qk(kd)
+    v8, vs = sage.sage_quant_v(vd)
+    _, codes = sage.sage_debug_p_codes(q8, qs, k8, ks, v8, vs, 1, S, H, D, 1.0 / math.sqrt(D))
+    torch.cuda.synchronize()
+    Sp = sage.sage_seq_pad(S)
+    p8 = codes.cpu().numpy()[0, 0]                                   # [S, Sp], natural key order
+    vt = np.zeros((D, Sp), np.uint8)
+    vt[:, :S] = unpermute_vt(v8[0:1, 0:1].cpu().numpy(), S)[0, 0].T  # [D, S] codes per channel
+    rng = np.random.default_rng(12)
+    rows = rng.choice(S, 64, replace=False)
+    # every (query, channel, block of 64 keys) of the sampled rows
+    a = np.ascontiguousarray(np.broadcast_to(vt.reshape(D, Sp // 64, 64)[None], (64, D, Sp // 64, 64)).reshape(-1, 64))
+    b = np.ascontiguousarray(np.broadcast_to(p8[rows].reshape(64, 1, Sp // 64, 64), (64, D, Sp // 64, 64)).reshape(-1, 64))
+    keep = b.any(axis=1)
+    _check_against_model(a[keep], b[keep], np.zeros(int(keep.sum()), np.float32), "V^T x P blocks of 64 keys")
