@@ -202,7 +202,8 @@ sage_status sage_attention(const void* q, const void* k, const void* v, int64_t 
  * of one (b, h), rows [r0, r0+nr) x keys [c0, c0+nc), computed through the
  * attention kernel's own path: K tiles staged into LDS by the same
  * buffer-to-LDS copies into the same swizzled layout, the same Q fragments,
- * the same INT8 MFMA sequence with the accumulators starting from zero.
+ * the same INT8 MFMA sequence with the accumulators starting from the same
+ * bias (0x4B400000, subtracted when a score is stored).
  *   scores  int32 [nr, nc] out, row-major.
  * Windows must satisfy 0 <= r0, 0 < nr, r0+nr <= S_pad (same for keys).
  * D is 128 or 64.

@@ -9,8 +9,13 @@
 // E4M3FN with the fixed scale 448 (the largest E4M3FN value), folded into the
 // exponent of exp2.
 //
-// The INT8 scores A (|A| < 2^21) are converted to fp32 exactly; the exponent
-// A * f - m2 is then formed with a single rounding (one fused multiply-add).
+// The INT8 score accumulators start at 0x4B400000, the bit pattern of the
+// fp32 value 1.5 * 2^23: since |A| < 2^21, the accumulated integer
+// 0x4B400000 + A is the bit pattern of the exact fp32 value 1.5 * 2^23 + A,
+// and integer order of the biased values is still score order. One exact
+// fp32 subtraction recovers A as a float (a full-rate instruction, where the
+// integer-to-float conversion is half rate); the exponent A * f - m2 is then
+// formed with a single rounding (one fused multiply-add).
 // The row sum l that normalizes the output is the sum of the decoded FP8 codes
 // of P (the weights PV applies), formed by the matrix cores: two more FP8
 // MFMAs per key tile with an all-ones A operand.
@@ -161,11 +166,14 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+constexpr int kScoreBias = 0x4B400000;        // bits of 1.5 * 2^23
+constexpr float kScoreBiasF = 12582912.0f;     // 1.5 * 2^23
+
 // P' = 2^fl32(A f - m2) for the 64 scores of a lane and their E4M3FN codes
 // packed in the FP8 MFMA B-operand order (byte 16 (u%2) + r of pop[u/2]
-// holds sub-tile u, register r). A converts to fp32 exactly (|A| < 2^24);
-// the exponent is then one fused multiply-add, i.e. the exact A f - m2
-// rounded once.
+// holds sub-tile u, register r). A is read from the biased accumulator
+// X = 1.5 * 2^23 + A as the exact difference X - 1.5 * 2^23; the exponent is
+// then one fused multiply-add, i.e. the exact A f - m2 rounded once.
 // kClamp: saturate before the conversion (the hardware conversion gives NaN
 // above 464). kTail: keys at or past `nvalid` get P' = 0. kDump: also store
 // the codes to prow[key] (key within the tile; debug builds of the kernel).
@@ -180,7 +188,8 @@ __device__ __forceinline__ void softmax_p(const v16i s[4], const float f[4], flo
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * j + e;
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[u][r], f[u], -m2));
+        const float a = __int_as_float(s[u][r]) - kScoreBiasF;   // exact
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(a, f[u], -m2));
         if (kTail && key_of(u, r, g) >= nvalid) pe = 0.0f;
         p[e] = kClamp ? fminf(pe, 448.0f) : pe;
       }
@@ -298,7 +307,9 @@ __device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const fl
   for (int u = 0; u < 4; ++u) f[u] = (qs * (u == 0 ? ks4.x : u == 1 ? ks4.y : u == 2 ? ks4.z : ks4.w)) * c;
 
   // t = fl32(A f) is monotone in A for f >= 0, so the tile max is taken on
-  // the integers of each 32-key block and dequantized once.
+  // the (biased) integers of each 32-key block and dequantized once: the
+  // biased maximum read as a float is 1.5 * 2^23 + A, and subtracting
+  // 1.5 * 2^23 is exact (both lie in [2^23, 2^24)).
   float tmax = -INFINITY;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -309,9 +320,9 @@ __device__ __forceinline__ void vector_phase(const v16i s[4], float qs, const fl
       for (int r = 0; r < 16; ++r)
         if (key_of(u, r, g) >= nvalid) sm[r] = INT32_MIN;
       const int mx = max16(sm);
-      if (mx != INT32_MIN) tmax = fmaxf(tmax, (float)mx * f[u]);
+      if (mx != INT32_MIN) tmax = fmaxf(tmax, (__int_as_float(mx) - kScoreBiasF) * f[u]);
     } else {
-      tmax = fmaxf(tmax, (float)max16(s[u]) * f[u]);
+      tmax = fmaxf(tmax, (__int_as_float(max16(s[u])) - kScoreBiasF) * f[u]);
     }
   }
   tmax = pair_max(tmax);
@@ -441,7 +452,12 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
     qs = qscale[bh * (Sq_pad / kQBlock) + q0 / kQBlock];
   }
 
-  const v16i bias = (v16i){0};   // score accumulators start from zero
+  v16i bias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bias[r] = kScoreBias;
+  // Opaque to the optimizer: the bias then stays in VGPRs for the whole loop
+  // instead of being copied from SGPRs before every tile.
+  asm volatile("" : "+v"(bias));
   RowState st{-INFINITY, -INFINITY};
   v16f lacc = (v16f){0};         // row sums of the codes (every register of a lane: its query)
   v8i ones;
@@ -557,7 +573,8 @@ void attn_fwd_kernel(const int8_t* __restrict__ q8, const float* __restrict__ qs
 // Debug dump of the int32 scores of one (b, h) through the attention
 // kernel's own path: K tiles staged into LDS by KvStage (buffer-to-LDS
 // copies into the swizzled slot), the wave's Q fragment in VGPRs, the INT8
-// MFMA sequence of qk_tile with accumulators starting from zero.
+// MFMA sequence of qk_tile with accumulators starting from the bias
+// 0x4B400000; the bias is subtracted when a score is stored.
 // grid (key tiles of the window, query tiles of kQueryTile rows), 8 waves.
 template <int kD>
 __global__ __launch_bounds__(64 * kAttnWaves) void debug_qk_kernel(const int8_t* __restrict__ q8,
@@ -577,9 +594,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void debug_qk_kernel(const int8_t*
   const int qa = rA + blockIdx.y * kQueryTile + wave * 32;
   v4i qf[kD / 32];
   load_q_frag<kD>(q8 + ((bh * S_pad + qa + li) * kD + (kD / 2) * g), qf);
-  const v16i zero = (v16i){0};
+  v16i bias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bias[r] = kScoreBias;
   v16i sacc[4];
-  qk_tile<kD>(lds_k, qf, li, g, zero, sacc);
+  qk_tile<kD>(lds_k, qf, li, g, bias, sacc);
   const int row = qa + li;
   if (row < r0 || row >= r0 + nr) return;
 #pragma unroll
@@ -588,7 +607,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void debug_qk_kernel(const int8_t*
     for (int r = 0; r < 16; ++r) {
       const int key = t * kKeyTile + key_of(u, r, g);
       if (key >= c0 && key < c0 + nc)
-        scores[(int64_t)(row - r0) * nc + (key - c0)] = sacc[u][r];
+        scores[(int64_t)(row - r0) * nc + (key - c0)] = sacc[u][r] - kScoreBias;
     }
 }
 
