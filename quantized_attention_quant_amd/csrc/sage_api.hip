@@ -434,8 +434,8 @@ sage_status sage_debug_p_codes(const int8_t* q_i8, const float* q_scale, const i
   if (!codes) return fail(SAGE_ERR_NULL, "codes is NULL");
   if (!(std::isfinite(softmax_scale) && softmax_scale >= 0.0f))
     return fail(SAGE_ERR_SHAPE, "softmax_scale must be finite and >= 0");
-  if (S > kDebugPMaxSeq) return fail(SAGE_ERR_RANGE, "S above %d (the code dump is S x S_pad bytes per head)",
-                                     kDebugPMaxSeq);
+  if (S > kDebugPMaxSeq) return fail(SAGE_ERR_RANGE, "S above %lld (the code dump is S x S_pad bytes per head)",
+                                     (long long)kDebugPMaxSeq);
   if (forced_launch_failure()) return fail(SAGE_ERR_HIP, "forced launch failure (SAGE_TEST_FAIL_LAUNCH)");
   const int nqt = (int)((S + sage::kQueryTile - 1) / sage::kQueryTile);
   const int64_t nwg = B * H * nqt;
