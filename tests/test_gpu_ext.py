@@ -95,6 +95,41 @@ def test_attn_fwd_ex_cross_and_lse(idx, Sq, Skv, H):
     lse_gate(lse.cpu().numpy(), rlse, f"Sq={Sq} Skv={Skv}")
 
 
+def _merge(parts):
+    """Attention over the union of key shards from per-shard outputs and
+    log-sum-exps (fp64): O = sum_i e^(lse_i) O_i / sum_i e^(lse_i)."""
+    lses = np.stack([np.transpose(l.astype(np.float64), (0, 2, 1))[..., None] for _, l in parts])   # [n,B,S,H,1]
+    m = lses.max(axis=0)
+    w = np.exp(lses - m)
+    outs = np.stack([o.astype(np.float64) for o, _ in parts])
+    return (w * outs).sum(axis=0) / w.sum(axis=0)
+
+
+@pytest.mark.parametrize("idx,Sq,splits,H", [(1, 300, (384, 316), 2), (3, 200, (256, 128, 333), 2)])
+def test_lse_merges_key_shards(idx, Sq, splits, H):
+    """The use the LSE output exists for (ring attention): attention over K/V
+    split into shards, each run on its own with its LSE, merged on the host.
+    The merge of the GPU shards equals the merge of the oracle's shards
+    within the output gate, and approximates exact attention over all keys."""
+    cfg = workloads.config(idx)
+    Skv = sum(splits)
+    _say(f"LSE merge config {idx} Sq={Sq} shards={splits} H={H}")
+    q, k, v = cross_inputs(idx, Sq, Skv, H, seed=1300 + Sq)
+    qd = to_dev(q)
+    gpu_parts, ref_parts = [], []
+    j0 = 0
+    for n in splits:
+        ks, vs = np.ascontiguousarray(k[:, j0:j0 + n]), np.ascontiguousarray(v[:, j0:j0 + n])
+        o, l = sage.sage_attention_ex(qd, to_dev(ks), to_dev(vs), cfg.softmax_scale, return_lse=True)
+        torch.cuda.synchronize()
+        gpu_parts.append((o.float().cpu().numpy(), l.cpu().numpy()))
+        ref_parts.append(oracle.sage_attention(q, ks, vs, cfg.softmax_scale, sage.sage_kv_tile(), return_lse=True))
+        j0 += n
+    got, ref = _merge(gpu_parts), _merge(ref_parts)
+    ex = oracle.exact_attention_fp64(q, k, v, cfg.softmax_scale)
+    gate(got, ref, ex, f"merged shards {splits}")
+
+
 def test_attn_fwd_ex_equal_lengths_is_attn_fwd():
     _say("attn_fwd_ex(S, S, lse=NULL) vs attn_fwd")
     q, k, v = workloads.generate(3, S=700, H=3, B=1, seed=41)
