@@ -28,6 +28,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -54,10 +55,16 @@ KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_quant_amd", "csrc", n)
 
 
 def kernel_hash() -> str:
+    """sha256 prefix of the attention kernel's code: its sources without
+    comments, whitespace collapsed, so that a comment edit keeps the
+    counters taken on the same code."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as fh:
-            h.update(fh.read())
+        with open(p) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -393,14 +393,14 @@ __device__ __forceinline__ void pv_tile(const uint8_t* lv, const v8i pop[2], int
 // that on each SIMD one wave's exp/FMA work meets the other wave's MFMAs:
 //   interval i, waves 0-3: softmax(i), QK(i+1), PV(i)
 //   interval i, waves 4-7: QK(i), PV(i-1), softmax(i)
-// (QK first, so that the row maxima of the new scores can be formed while
-// the PV MFMAs run)
+// (waves 4-7 issue QK first because their vector phase needs its scores;
+// the PV MFMAs issued after them are still in the pipe when it starts)
 // (waves 0-3 compute QK(0) before interval 0; waves 4-7 compute PV(T-1)
 // after the last one). The matrix phase runs at raised wave priority
 // (s_setprio 2): its few MFMA and LDS issues then go first, and the other
-// wave's vector work fills the cycles between them. Interval i reads K tiles i, i+1 and V tiles i-1, i,
-// and loads K tile i+2 and V tile i+1 into the third slot of each
-// three-stage LDS ring.
+// wave's vector work fills the cycles between them. Interval i reads K
+// tiles i, i+1 and V tiles i-1, i, and loads K tile i+2 and V tile i+1 into
+// the third slot of each three-stage LDS ring.
 // kDump (debug instantiation): the P codes of every tile are also stored to
 // pdump [B, H, Sq, Skv_pad] (key order; padded keys 0).
 template <int kD, bool kQuantQ, bool kDump = false>
