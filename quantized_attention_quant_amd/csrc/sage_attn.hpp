@@ -126,7 +126,7 @@ __device__ __forceinline__ void quant_q_frag(const uint16_t* __restrict__ qraw, 
 
 // S^T for the 128 keys of the staged tile against the wave's 32 queries:
 // sacc[u] covers keys [32 u, 32 u + 32) of the tile; every accumulator
-// starts from `init` (zero).
+// starts from `init` (the score bias).
 template <int kD>
 __device__ __forceinline__ void qk_tile(const uint8_t* __restrict__ lds_k, const v4i qf[kD / 32], int li, int g,
                                         const v16i& init, v16i sacc[4]) {
