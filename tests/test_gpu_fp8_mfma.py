@@ -198,3 +198,78 @@ def test_fp8_mfma_on_attention_codes():
     b = np.ascontiguousarray(np.broadcast_to(p8[rows].reshape(64, 1, Sp // 64, 64), (64, D, Sp // 64, 64)).reshape(-1, 64))
     keep = b.any(axis=1)
     _check_against_model(a[keep], b[keep], np.zeros(int(keep.sum()), np.float32), "V^T x P blocks of 64 keys")
+
+
+def _rowsum_key_groups():
+    """The 8-key groups in which the attention kernel's row-sum MFMAs see a
+    128-key tile: MFMA w covers sub-tiles 2w and 2w + 1; lane half g holds
+    keys 32u + 8j + 4g + e (e < 4) in byte 4 (4 (u % 2) + j) + e of its 32
+    operand bytes, and each 8 consecutive bytes form a group."""
+    groups = []
+    for w in range(2):
+        for g in range(2):
+            for q in range(4):
+                keys = []
+                for d in (2 * q, 2 * q + 1):
+                    u, j = 2 * w + d // 4, d % 4
+                    keys += [32 * u + 8 * j + 4 * g + e for e in range(4)]
+                groups.append(keys)
+    return np.array(groups)
+
+
+def test_lse_equals_the_row_sum_mfma_model():
+    """The kernel's LSE against a model of its own arithmetic: the row sum l
+    rebuilt from the kernel's P codes, grouped as its row-sum MFMAs see them
+    and cut by the rule pinned above, each tile scaled by 2^(m2_tile - m2_last).
+    Agreement within fp32 rounding alone (no allowance for the cut) shows that
+    the LSE differs from the oracle's exact sum of codes by that rule only."""
+    say("LSE against the row-sum MFMA model (outlier recipe, S=600)")
+    S, H, D = 600, 2, 128
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = workloads.generate(3, S=S, H=H, B=1, seed=11)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    q8, qs = sage.sage_quant_qk(qd)
+    k8, ks = sage.sage_quant_qk(kd)
+    v8, vs = sage.sage_quant_v(vd)
+    _, codes = sage.sage_debug_p_codes(q8, qs, k8, ks, v8, vs, 1, S, H, D, scale)
+    _, lse = sage.sage_attn_fwd_ex(q8, qs, k8, ks, v8, vs, 1, S, S, H, D, scale, return_lse=True)
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy()
+    lse = lse.cpu().numpy().astype(np.float64)
+    oq, oqs = oracle.quant_qk(q)
+    ok, oks = oracle.quant_qk(k)
+    ov, _ = oracle.quant_v(v)
+    groups = _rowsum_key_groups()
+    c = oracle.exp2_scale(scale)
+    blk = np.arange(S) // 32
+    for h in range(H):
+        A = oracle.qk_scores(oq[0, h], ok[0, h])
+        f = ((oqs[0, h][:, None].astype(np.float32) * oks[0, h][None, :].astype(np.float32)).astype(np.float32)
+             * c).astype(np.float32)[blk[:, None], blk[None, :]]
+        trace = []
+        oracle.online_softmax_pv(A, f, oracle.fp8_e4m3fn_decode(ov[0, h]), 128, trace=trace)
+        m2_last = trace[-1]["m2"].astype(np.float64)
+        l_model = np.zeros(S)
+        flips = 0
+        for t in trace:
+            j0 = t["j0"]
+            tile = codes[0, h, :, j0:j0 + 128]                      # [S, 128], keys past S are 0
+            flips += int(np.count_nonzero(tile[:, :t["j1"] - j0] != t["p8"]))
+            g8 = tile[:, groups]                                    # [S, 16, 8]
+            n = g8.shape[0] * g8.shape[1]
+            a = np.full((n, 64), _code(1.0), np.uint8)
+            b = np.zeros((n, 64), np.uint8)
+            b[:, :8] = g8.reshape(n, 8)
+            tile_sum, _ = model_dot(a, b, np.zeros(n, np.float32))
+            l_model += tile_sum.reshape(S, 16).sum(axis=1) * np.exp2(t["m2"].astype(np.float64) - m2_last)
+        lse_model = np.log(2.0) * (m2_last + np.log2(l_model))
+        r = 4e-5 + 1e-6 * np.abs(lse_model)
+        d = lse[0, h] - lse_model
+        exact = oracle.lse_from_state(m2_last, np.sum([oracle.fp8_e4m3fn_decode(codes[0, h, :, t["j0"]:t["j0"] + 128])
+                                                       .astype(np.float64).sum(axis=1)
+                                                       * np.exp2(t["m2"].astype(np.float64) - m2_last)
+                                                       for t in trace], axis=0))
+        say(f"  h={h}: lse - model in [{d.min():.3g}, {d.max():.3g}] (r <= {r.max():.3g}); "
+            f"model - exact code sum in [{(lse_model - exact).min():.3g}, {(lse_model - exact).max():.3g}]; "
+            f"code flips against the oracle {flips}")
+        assert np.all(np.abs(d) <= r), h
