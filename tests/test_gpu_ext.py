@@ -144,6 +144,28 @@ def test_attn_fwd_ex_equal_lengths_is_attn_fwd():
     assert bool(torch.isfinite(lse).all())
 
 
+@pytest.mark.parametrize("idx,S,H,B,parts", [(2, 1000, 4, 1, 2), (5, 333, 6, 2, 3)])
+def test_head_shards_are_bit_identical(idx, S, H, B, parts):
+    """A head-sharded run, one GPU's share under Ulysses context parallelism
+    (diffusers PR #15060, "What does this PR do?"), gives bit for bit the
+    heads of the full run: every (b, h) is quantized and attended on its own
+    (the Q/K blocks lie inside one head, V's scale is per (b, h, channel),
+    the softmax per row), so no result depends on the other heads."""
+    cfg = workloads.config(idx)
+    _say(f"head shards config {idx} B={B} S={S} H={H} parts={parts}")
+    q, k, v = workloads.generate(idx, S=S, H=H, B=B, seed=880 + S)
+    full, lse = sage.sage_attention_ex(to_dev(q), to_dev(k), to_dev(v), cfg.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    hs = H // parts
+    for p in range(parts):
+        sl = slice(p * hs, (p + 1) * hs)
+        qs_, ks_, vs_ = (np.ascontiguousarray(x[:, :, sl, :]) for x in (q, k, v))
+        o, l = sage.sage_attention_ex(to_dev(qs_), to_dev(ks_), to_dev(vs_), cfg.softmax_scale, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, full[:, :, sl, :]), f"shard {p}: output differs"
+        assert torch.equal(l, lse[:, sl, :]), f"shard {p}: LSE differs"
+
+
 # --------------------------------------------------------------------------
 # one-shot entry point
 
