@@ -4,15 +4,17 @@
  *
  * What it computes (diffusers issue #15014, "gfx1201 (RDNA4) SageAttention
  * attention backend: aiter package or Hub kernel?", problem statement): the
- * forward of softmax(Q K^T * softmax_scale) V with INT8 QK^T and FP8 PV, FP32
- * accumulation, Q and K quantized per 32-row block and V per channel, on bf16
- * [B, S, H, 128] inputs of equal shape, with no mask and no causality. The
+ * forward of softmax(Q K^T * softmax_scale) V where QK^T multiplies INT8
+ * codes and PV FP8 codes, both summing in fp32, with one scale per 32-row
+ * block of Q and of K and one per channel of V, on bf16 [B, S, H, 128]
+ * inputs of one shape, unmasked and non-causal. The
  * call there is gfx1201_sage_attention(q, k, v, softmax_scale). Inference
  * only, and no log-sum-exp is returned (diffusers PR #15060, "Add
  * aiter_sage_hub attention backend for AMD RDNA4 (gfx1201)", section "What
  * does this PR do?"). Unsupported inputs are rejected with an error code
- * rather than served differently (the issue's "Describe the solution you'd
- * like": reject with a clear error); a caller may fall back on its own.
+ * rather than served differently (the issue's section "Describe the
+ * solution you'd like" asks for an explicit failure there); a caller may
+ * fall back on its own.
  *
  * Conventions for every entry point:
  *   - Every tensor pointer is a device pointer owned by the caller. The
@@ -90,7 +92,7 @@ size_t sage_workspace_bytes(int64_t B, int64_t S, int64_t H, int64_t D);
 
 /*
  * sage_quant_qk - INT8 quantization of Q or K per 32-row block (issue #15014,
- * problem statement: "Q/K are quantized per 32-row block").
+ * problem statement: one scale per 32-row block of Q and of K).
  *   x       bf16 [B, S, H, D], contiguous (row (b, s, h) holds D values).
  *   x_i8    int8 [B, H, S_pad, D] out, S_pad = sage_seq_pad(S); rows >= S
  *           are written as zeros.
@@ -106,7 +108,7 @@ sage_status sage_quant_qk(const void* x, int64_t B, int64_t S, int64_t H, int64_
 
 /*
  * sage_quant_v - FP8 E4M3FN quantization of V per channel (issue #15014,
- * problem statement: "V per channel").
+ * problem statement: one scale per channel of V).
  *   v        bf16 [B, S, H, D], contiguous.
  *   v_fp8_t  uint8 [B, H, D, S_pad] out: OCP E4M3FN codes, transposed (one
  *            row of S_pad keys per channel). Within each group of 64 keys
@@ -161,7 +163,7 @@ sage_status sage_quant_v_noalloc(const void* v, int64_t B, int64_t S, int64_t H,
 
 /*
  * sage_attn_fwd - fused attention on quantized inputs (issue #15014,
- * problem statement: INT8 QK^T and FP8 PV with FP32 accumulation).
+ * problem statement: QK^T on INT8 codes, PV on FP8 codes, fp32 sums).
  * Inputs are the outputs of sage_quant_qk (Q and K) and sage_quant_v.
  * out: bf16 [B, S, H, D] (the input layout), rows >= S are not written.
  * Per query row i, over key tiles of sage_kv_tile() keys in key order:

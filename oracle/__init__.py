@@ -19,9 +19,10 @@ order the method states it, written for a reader to check by eye:
 Sources (cited by page title and section throughout):
 
 * diffusers issue #15014, "gfx1201 (RDNA4) SageAttention attention backend:
-  aiter package or Hub kernel?", problem statement: INT8 QK^T and FP8 PV with
-  FP32 accumulation; Q/K quantized per 32-row block and V per channel inside
-  the kernel; bf16 [B, S, H, 128] inputs, equal Q/K/V shapes, no mask,
+  aiter package or Hub kernel?", problem statement: QK^T multiplies INT8
+  codes and PV FP8 codes, both summing in fp32; the kernel itself gives Q and
+  K one scale per 32 sequence rows and V one scale per channel; the inputs
+  are bf16 [B, S, H, 128], one shape for Q, K and V, unmasked and
   non-causal. The operation is ``gfx1201_sage_attention(q, k, v, softmax_scale)``.
 * diffusers PR #15060, "Add aiter_sage_hub attention backend for AMD RDNA4
   (gfx1201)", section "What does this PR do?": inference only, no LSE.

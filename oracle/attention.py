@@ -3,8 +3,9 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Source: diffusers issue #15014, "gfx1201 (RDNA4) SageAttention attention
-backend: aiter package or Hub kernel?", problem statement: INT8 QK^T and FP8
-PV with FP32 accumulation, bf16 [B, S, H, 128] inputs, no mask, non-causal,
+backend: aiter package or Hub kernel?", problem statement: QK^T on INT8 codes
+and PV on FP8 codes, each summed in fp32, over bf16 [B, S, H, 128] inputs
+without a mask or causality,
 operation ``gfx1201_sage_attention(q, k, v, softmax_scale)``; diffusers PR
 #15060, "What does this PR do?": no LSE is returned.
 

@@ -3,9 +3,9 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Source: diffusers issue #15014, "gfx1201 (RDNA4) SageAttention attention
-backend: aiter package or Hub kernel?", problem statement: Q and K are
-quantized per 32-row block and V per channel, inside the kernel, for INT8
-QK^T and FP8 PV. InvokeAI PR #9657, section "How it works": no K smoothing.
+backend: aiter package or Hub kernel?", problem statement: the kernel itself
+gives Q and K one INT8 scale per block of 32 rows and V one FP8 scale per
+channel, feeding an INT8 QK^T and an FP8 PV. InvokeAI PR #9657, section "How it works": no K smoothing.
 
 Readings taken where the pages are silent:
 

@@ -1,8 +1,9 @@
 // Fused attention forward on quantized inputs for gfx950.
 //
 // Source: diffusers issue #15014, "gfx1201 (RDNA4) SageAttention attention
-// backend: aiter package or Hub kernel?", problem statement: INT8 QK^T and
-// FP8 PV with FP32 accumulation, bf16 [B, S, H, 128], no mask, non-causal.
+// backend: aiter package or Hub kernel?", problem statement: QK^T on INT8
+// codes and PV on FP8 codes, both summed in fp32, over bf16 [B, S, H, 128]
+// without a mask or causality.
 // Also instantiated for head dim 64, and for query and key sequences of
 // different lengths, with an optional per-row log-sum-exp.
 // The online (flash-style) softmax streams key tiles; P is quantized to FP8

@@ -1,8 +1,9 @@
 // Quantization pre-pass kernels: INT8 Q/K per 32-row block, FP8 V per channel.
 //
 // Source: diffusers issue #15014, "gfx1201 (RDNA4) SageAttention attention
-// backend: aiter package or Hub kernel?", problem statement (Q/K per 32-row
-// block, V per channel, INT8 QK^T and FP8 PV). Both passes are bound by HBM
+// backend: aiter package or Hub kernel?", problem statement: one scale per
+// 32 rows of Q and of K, one per channel of V, feeding an INT8 score product
+// and an FP8 value product. Both passes are bound by HBM
 // bandwidth: each reads its bf16 input once (V twice: amax, then quantize)
 // and writes one byte per element.
 #pragma once

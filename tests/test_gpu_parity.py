@@ -341,8 +341,8 @@ def test_huge_scores_saturate_like_the_oracle():
 
 
 def _magnitude_inputs(kind, S, H, seed):
-    """Large-magnitude Q/K: the pages' outlier statistics (a Q/K channel near
-    600 for all image tokens, InvokeAI PR #9657, "How it works") and uniform
+    """Large-magnitude Q/K: the pages' outlier statistics (one Q/K channel of
+    about 600 on every image token, InvokeAI PR #9657, "How it works") and uniform
     scalings that put whole blocks at outlier scale."""
     if kind == "c3":
         return workloads.generate(3, S=S, H=H, seed=seed)

@@ -10,8 +10,9 @@ Qwen-Image, Wan); none of those weights are available, so these recipes stand
 in for them. They use the attention shapes the pages name (bf16 [B, S, H, 128],
 self-attention, equal Q/K/V shapes: diffusers issue #15014, "gfx1201 (RDNA4)
 SageAttention attention backend: aiter package or Hub kernel?", problem
-statement) and the outlier structures the pages describe (a Q/K channel near
-600 for all image tokens and V near 3500 in every channel: InvokeAI PR #9657,
+statement) and the outlier structures the pages describe (one Q/K channel of
+about 600 on every image token, and V values of about 3500 across the
+channels: InvokeAI PR #9657,
 "feat(attention): add opt-in SageAttention backend for diffusion models",
 sections "How it works" and "Remaining risks").
 
