@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests run only when a GPU is visible; on a CPU host they are skipped
-    # (the driver deselects them with -m "not gpu" anyway).
+    # (a CPU run normally deselects them with -m "not gpu" as well).
     try:
         import torch
         has_gpu = torch.cuda.is_available()
