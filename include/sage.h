@@ -226,7 +226,8 @@ sage_status sage_debug_qk_scores(const int8_t* q_i8, const int8_t* k_i8, int64_t
  *            receives the same output bit for bit).
  *   codes    uint8 [B, H, S, S_pad] out, caller-owned: codes[b,h,i,j] is the
  *            code of query i and key j (natural key order); keys >= S are 0.
- * S <= 16384 (SAGE_ERR_RANGE otherwise). Test and diagnostic use only.
+ * S <= 131072 (SAGE_ERR_RANGE otherwise): the codes take S * S_pad bytes
+ * per (b, h), up to 17 GB. Test and diagnostic use only.
  */
 sage_status sage_debug_p_codes(const int8_t* q_i8, const float* q_scale, const int8_t* k_i8,
                                const float* k_scale, const uint8_t* v_fp8_t, const float* v_scale,

@@ -24,7 +24,7 @@ static __device__ __align__(256) uint8_t scratch[SAGE_NOALLOC_SCRATCH_BYTES];
 namespace {
 
 constexpr int kAbiVersion = 1;
-constexpr int64_t kDebugPMaxSeq = 16384;  // sage_debug_p_codes: S x S_pad bytes per head
+constexpr int64_t kDebugPMaxSeq = 131072;  // sage_debug_p_codes: S x S_pad bytes per head
 constexpr int64_t kDebugDotMax = int64_t(1) << 24;  // sage_debug_fp8_dot pairs
 thread_local char g_last_error[512] = "";
 

@@ -122,7 +122,7 @@ def test_validation_codes():
     c01 = ctypes.c_float(0.1)
     assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 256, 2, 128, c01, z, f, z) == ERR_NULL
     assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 256, 2, 96, c01, f, f, z) == ERR_UNSUP
-    assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 16385, 2, 128, c01, f, f, z) == ERR_RANGE
+    assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 131073, 2, 128, c01, f, f, z) == ERR_RANGE
     assert _call("sage_debug_p_codes", f, f, f, f, f, f, 1, 256, 2, 128, ctypes.c_float(-1.0), f, f, z) == ERR_SHAPE
     assert _call("sage_debug_p_codes", m, f, f, f, f, f, 1, 256, 2, 128, c01, f, f, z) == ERR_ALIGN
     # FP8 MFMA probe: pointers, alignment, pair count

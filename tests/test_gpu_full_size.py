@@ -124,3 +124,48 @@ def test_attention_sampled_rows_and_lse(workload):
         ex = exact_rows(q, k, v, b, h, rows, cfg.softmax_scale)
         gate(g, ref, ex, f"workload {idx} (b,h)=({b},{h}) rows={len(rows)}")
         lse_gate(lse[b, h, ti].cpu().numpy(), rl, f"workload {idx} (b,h)=({b},{h})")
+
+
+def test_p_codes_on_sampled_rows(workload):
+    """The FP8 codes of P at full size: one head of the workload through the
+    debug instantiation of the attention kernel (its output equals
+    sage_attn_fwd's bit for bit), against the oracle's tile loop on sampled
+    query rows (first, last and random 32-row blocks, and the head's 32 rows
+    of largest |Q|, which in the outlier recipe are the x8 rows). A code may
+    differ only by one step, after an fp32 rounding difference of the exp2;
+    at most 1e-4 of them may."""
+    idx, (q, k, v), _ = workload
+    cfg = workloads.config(idx)
+    b, h = 0, cfg.H - 1
+    S, D = cfg.S, cfg.D
+    say(f"P codes at full size, workload {idx}, (b,h)=({b},{h}), S={S}")
+    qh, kh, vh = (_head(x, b, h) for x in (q, k, v))
+    q8, qs = sage.sage_quant_qk(to_dev(qh))
+    k8, ks = sage.sage_quant_qk(to_dev(kh))
+    v8, vs = sage.sage_quant_v(to_dev(vh))
+    plain = sage.sage_attn_fwd(q8, qs, k8, ks, v8, vs, 1, S, 1, D, cfg.softmax_scale)
+    out, codes = sage.sage_debug_p_codes(q8, qs, k8, ks, v8, vs, 1, S, 1, D, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+    rng = np.random.default_rng(70 + idx)
+    nb = (S + 31) // 32
+    blocks = sorted(set([0, nb - 1] + list(rng.choice(nb, 4, replace=False))))
+    top = np.argsort(np.abs(qh[0, :, 0, :]).max(axis=1))[-32:]
+    rows = np.unique(np.concatenate([np.arange(32 * t, min(S, 32 * t + 32)) for t in blocks] + [top]))
+    got = codes[0, 0][torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    assert np.all(got[:, S:] == 0)
+    oq, oqs = oracle.quant_qk(qh)
+    ok, oks = oracle.quant_qk(kh)
+    ov, _ = oracle.quant_v(vh)
+    A = oracle.qk_scores(oq[0, 0][rows], ok[0, 0])
+    c = oracle.exp2_scale(cfg.softmax_scale)
+    fb = (oqs[0, 0][rows // 32][:, None].astype(np.float32) * oks[0, 0][None, :].astype(np.float32)).astype(np.float32)
+    f = (fb * c).astype(np.float32)[:, np.arange(S) // 32]
+    trace = []
+    oracle.online_softmax_pv(A, f, oracle.fp8_e4m3fn_decode(ov[0, 0]), sage.sage_kv_tile(), trace=trace)
+    ref = np.concatenate([t["p8"] for t in trace], axis=1)
+    d = got[:, :S].astype(np.int64) - ref.astype(np.int64)
+    flips = int(np.count_nonzero(d))
+    say(f"  P codes: {flips} of {d.size} differ from the oracle's ({flips / d.size:.2e}) on {len(rows)} rows")
+    assert np.abs(d).max() <= 1
+    assert flips <= 1e-4 * d.size
