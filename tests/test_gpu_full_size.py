@@ -133,7 +133,8 @@ def test_p_codes_on_sampled_rows(workload):
     query rows (first, last and random 32-row blocks, and the head's 32 rows
     of largest |Q|, which in the outlier recipe are the x8 rows). A code may
     differ only by one step, after an fp32 rounding difference of the exp2;
-    at most 1e-4 of them may."""
+    at most 1e-4 of them may. The kernel's LSE of those rows is then held to
+    the row-sum MFMA model of those codes within fp32 rounding alone."""
     idx, (q, k, v), _ = workload
     cfg = workloads.config(idx)
     b, h = 0, cfg.H - 1
@@ -169,3 +170,26 @@ def test_p_codes_on_sampled_rows(workload):
     say(f"  P codes: {flips} of {d.size} differ from the oracle's ({flips / d.size:.2e}) on {len(rows)} rows")
     assert np.abs(d).max() <= 1
     assert flips <= 1e-4 * d.size
+    # The LSE of the same rows against the row-sum MFMA model built from
+    # these codes: grouped as the kernel's row-sum MFMAs see them, cut by the
+    # rule test_gpu_fp8_mfma.py pins, each tile scaled by 2^(m2_tile - m2_last).
+    from test_gpu_fp8_mfma import _code, _rowsum_key_groups, model_dot
+    _, lse = sage.sage_attn_fwd_ex(q8, qs, k8, ks, v8, vs, 1, S, S, 1, D, cfg.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    lse_rows = lse[0, 0][torch.as_tensor(rows, device=DEV)].cpu().numpy().astype(np.float64)
+    groups = _rowsum_key_groups()
+    m2_last = trace[-1]["m2"].astype(np.float64)
+    R = len(rows)
+    l_model = np.zeros(R)
+    ones = np.full((R * 16, 64), _code(1.0), np.uint8)
+    for t in trace:
+        g8 = got[:, t["j0"]:t["j0"] + 128][:, groups]          # [R, 16, 8], keys past S hold 0
+        b8 = np.zeros((R * 16, 64), np.uint8)
+        b8[:, :8] = g8.reshape(R * 16, 8)
+        tile_sum, _ = model_dot(ones, b8, np.zeros(R * 16, np.float32))
+        l_model += tile_sum.reshape(R, 16).sum(axis=1) * np.exp2(t["m2"].astype(np.float64) - m2_last)
+    lse_model = np.log(2.0) * (m2_last + np.log2(l_model))
+    r = 4e-5 + 1e-6 * np.abs(lse_model)
+    dl = lse_rows - lse_model
+    say(f"  LSE - row-sum MFMA model in [{dl.min():.3g}, {dl.max():.3g}] (r <= {r.max():.3g}) over {len(trace)} tiles")
+    assert np.all(np.abs(dl) <= r)
