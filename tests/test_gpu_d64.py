@@ -14,7 +14,7 @@ import workloads
 
 torch = pytest.importorskip("torch")
 sage = pytest.importorskip("quantized_attention_quant_amd")
-from gpu_common import DEV, gate, kappa, lse_gate, say, to_dev  # noqa: E402
+from gpu_common import DEV, check_p_codes_and_models, gate, kappa, lse_gate, say, to_dev  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 D = 64
@@ -127,3 +127,14 @@ def test_debug_scores_d64():
         torch.cuda.synchronize()
         ref = oracle.qk_scores(oq[0, 1], ok[0, 1])[r0:r0 + nr, c0:c0 + nc]
         assert np.array_equal(got.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("idx,S", [(3, 16384), (5, 4000)])
+def test_p_codes_and_models_d64(idx, S):
+    """Head dim 64 at a large S: the FP8 codes of P, the LSE and the output of
+    one head against the oracle's tile loop and the FP8 MFMA model, on sampled
+    rows (gpu_common.check_p_codes_and_models)."""
+    say(f"D=64 P codes and models, recipe {idx}, S={S}: generating inputs")
+    q, k, v = workloads.generate(idx, S=S, H=1, B=1, seed=990 + S)
+    q, k, v = (np.ascontiguousarray(x[..., :64]) for x in (q, k, v))
+    check_p_codes_and_models(q, k, v, 1.0 / math.sqrt(64), np.random.default_rng(idx), f"D=64 recipe {idx}")
