@@ -15,7 +15,7 @@ import workloads
 
 torch = pytest.importorskip("torch")
 sage = pytest.importorskip("quantized_attention_quant_amd")
-from gpu_common import DEV, gate, lse_gate, say, to_dev  # noqa: E402
+from gpu_common import DEV, exact_rows, gate, lse_gate, oracle_rows, say, to_dev  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -205,3 +205,25 @@ def test_attn_fwd_qbf16_equals_split_path(D, Sq, Skv, H):
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     assert torch.equal(la, lb)
+
+
+@pytest.mark.parametrize("idx,Sq,Skv,H", [(3, 2048, 16384, 2), (5, 16384, 1000, 2)])
+def test_cross_attention_large_sampled_rows(idx, Sq, Skv, H):
+    """Cross-attention at large lengths (many key tiles against few query
+    tiles and the reverse), through the one-shot entry point with the LSE,
+    on sampled query rows against the oracle, under the stated gates."""
+    cfg = workloads.config(idx)
+    _say(f"large cross-attention config {idx} Sq={Sq} Skv={Skv} H={H}")
+    q, k, v = cross_inputs(idx, Sq, Skv, H, seed=1300 + Sq)
+    out, lse = sage.sage_attention_ex(to_dev(q), to_dev(k), to_dev(v), cfg.softmax_scale, return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(Sq + Skv)
+    bn = sage.sage_kv_tile()
+    for h in range(H):
+        rows = np.unique(np.concatenate([np.arange(32), np.arange(Sq - 32, Sq), rng.choice(Sq, 192, replace=False)]))
+        ti = torch.as_tensor(rows, device=DEV)
+        got = out[0, ti, h, :].float().cpu().numpy()
+        ref, rl = oracle_rows(q, k, v, 0, h, rows, cfg.softmax_scale, bn, return_lse=True)
+        ex = exact_rows(q, k, v, 0, h, rows, cfg.softmax_scale)
+        gate(got, ref, ex, f"cross {Sq}x{Skv} h={h} rows={len(rows)}")
+        lse_gate(lse[0, h, ti].cpu().numpy(), rl, f"cross {Sq}x{Skv} h={h}")
