@@ -227,3 +227,26 @@ def test_cross_attention_large_sampled_rows(idx, Sq, Skv, H):
         ex = exact_rows(q, k, v, 0, h, rows, cfg.softmax_scale)
         gate(got, ref, ex, f"cross {Sq}x{Skv} h={h} rows={len(rows)}")
         lse_gate(lse[0, h, ti].cpu().numpy(), rl, f"cross {Sq}x{Skv} h={h}")
+
+
+@pytest.mark.parametrize("idx,S,H", [(2, 4096, 2), (5, 16384, 1)])
+def test_smoothed_attention_large_sampled_rows(idx, S, H):
+    """K smoothing in the one-shot entry point at large S, on sampled query
+    rows against the oracle with smoothing, output and LSE under the stated
+    gates; the recipes carry K channel offsets, the case smoothing is for."""
+    cfg = workloads.config(idx)
+    _say(f"smoothed attention config {idx} S={S} H={H}")
+    q, k, v = workloads.generate(idx, S=S, H=H, B=1, seed=1700 + S)
+    out, lse = sage.sage_attention_ex(to_dev(q), to_dev(k), to_dev(v), cfg.softmax_scale, flags=sage.SAGE_SMOOTH_K,
+                                      return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(S)
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(S - 32, S), rng.choice(S, 192, replace=False)]))
+    ref, rl = oracle.sage_attention(q, k, v, cfg.softmax_scale, sage.sage_kv_tile(), rows=rows, smooth_k=True,
+                                    return_lse=True)
+    ti = torch.as_tensor(rows, device=DEV)
+    for h in range(H):
+        got = out[0, ti, h, :].float().cpu().numpy()
+        ex = exact_rows(q, k, v, 0, h, rows, cfg.softmax_scale)
+        gate(got, ref[0, rows, h, :], ex, f"smoothed S={S} h={h} rows={len(rows)}")
+        lse_gate(lse[0, h, ti].cpu().numpy(), rl[0, h, rows], f"smoothed S={S} h={h}")
