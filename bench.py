@@ -282,7 +282,7 @@ def main():
     pre_bytes = 8.0 * cfg.numel
     pre_avg = float(np.mean(pre_ms))
     result = {
-        "metric": "sage_attn_fwd effective TOPS at B1 S16384 H24 D128; % of MFMA peak",
+        "metric": f"sage_attn_fwd effective TOPS at B{B} S{S} H{H} D{D}; % of MFMA peak",
         "value": round(value, 2),
         "unit": "TOPS",
         "n_gpus": 1,
